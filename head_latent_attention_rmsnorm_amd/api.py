@@ -1,0 +1,256 @@
+"""Thin PyTorch binding of libmla (include/mla.h), one function per C entry
+point and with the same names. Argument marshalling only: device buffers are
+torch tensors, the stream is torch's current HIP stream, and every step of the
+path runs in the library's HIP kernels. Outputs not supplied by the caller are
+allocated with torch (the library itself never allocates).
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import DTYPE_BF16, DTYPE_FP16, PAIR_HALF, PAIR_INTERLEAVED, ROPE_DEFAULT, ROPE_YARN, RopeParams, check
+
+__all__ = [
+    "RopeParams", "rope_params", "mla_rope_table_build", "mla_softmax_scale", "mla_latent_rmsnorm",
+    "mla_kv_expand", "mla_prefill_attention", "mla_decode_attention", "pairing_code",
+    "PAIR_HALF", "PAIR_INTERLEAVED", "ROPE_DEFAULT", "ROPE_YARN",
+]
+
+
+def rope_params(kind: str, rope_dim: int, base: float, factor: float = 1.0, original_max_pos: int = 4096,
+                beta_fast: float = 32.0, beta_slow: float = 1.0, mscale: float = 1.0,
+                mscale_all_dim: float = 0.0) -> RopeParams:
+    """`mla_rope_params` from plain values; kind is "default" or "yarn"
+    (any other kind is passed as an unknown type and rejected by the library)."""
+    t = {"default": ROPE_DEFAULT, "yarn": ROPE_YARN}.get(kind, 99)
+    return RopeParams(int(rope_dim), t, float(base), float(factor), int(original_max_pos), float(beta_fast),
+                      float(beta_slow), float(mscale), float(mscale_all_dim))
+
+
+def params_from(spec, rope_dim: int) -> RopeParams:
+    """`mla_rope_params` from any object with the RopeSpec attributes."""
+    return rope_params(spec.kind, rope_dim, spec.base, spec.factor, spec.original_max_pos, spec.beta_fast,
+                       spec.beta_slow, spec.mscale, spec.mscale_all_dim)
+
+
+def pairing_code(pairing) -> int:
+    if isinstance(pairing, int):
+        return pairing
+    return {"half": PAIR_HALF, "interleaved": PAIR_INTERLEAVED}.get(pairing, 99)
+
+
+_DTYPE_CODE = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_FP16}
+
+
+def _kv_code(t: torch.Tensor, name: str) -> int:
+    """mla_dtype of a key/value tensor (bf16 or fp16)."""
+    if t.dtype not in _DTYPE_CODE:
+        raise TypeError(f"{name} must be bfloat16 or float16 (got {t.dtype})")
+    return _DTYPE_CODE[t.dtype]
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _shape(t: torch.Tensor, name: str, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} should be of size {tuple(shape)}, but is {tuple(t.shape)}")
+
+
+def _need(t: torch.Tensor, name: str, dtype=torch.bfloat16) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def mla_softmax_scale(rope: RopeParams, qk_head_dim: int) -> float:
+    out = ctypes.c_double()
+    check("mla_softmax_scale", _lib.load().mla_softmax_scale(ctypes.byref(rope), int(qk_head_dim), ctypes.byref(out)))
+    return out.value
+
+
+def mla_rope_table_build(rope: RopeParams, n_pos: int, device="cuda") -> Tuple[torch.Tensor, torch.Tensor, float]:
+    """cos, sin fp32 [n_pos, rope_dim/2] on `device`, and the softmax-scale
+    multiplier mscale(factor, mscale_all_dim)^2 (1 when not applicable)."""
+    lib = _lib.load()
+    half = rope.rope_dim // 2
+    cos = torch.empty((n_pos, half), dtype=torch.float32, device=device)
+    sin = torch.empty((n_pos, half), dtype=torch.float32, device=device)
+    m2 = ctypes.c_double()
+    check("mla_rope_table_build",
+          lib.mla_rope_table_build(ctypes.byref(rope), int(n_pos), _ptr(cos), _ptr(sin), ctypes.byref(m2),
+                                   _stream(cos)))
+    return cos, sin, m2.value
+
+
+def mla_latent_rmsnorm(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """RMSNorm over the last dim of x (bf16 [..., R]) with weight w (bf16 [R]);
+    returns the normalised latent in fp32 [..., R]."""
+    _need(x, "x")
+    _need(w, "w")
+    R = x.shape[-1]
+    if w.numel() != R:
+        raise ValueError("weight size does not match the latent width")
+    y = torch.empty(x.shape, dtype=torch.float32, device=x.device) if out is None else out
+    _need(y, "out", torch.float32)
+    _shape(y, "out", x.shape)
+    n = x.numel() // R if R else 0
+    check("mla_latent_rmsnorm",
+          _lib.load().mla_latent_rmsnorm(_ptr(x), _ptr(w), float(eps), _ptr(y), n, R, _stream(x)))
+    return y
+
+
+def mla_kv_expand(c_norm: torch.Tensor, W: torch.Tensor, H: int, Dn: int, Dv: int,
+                  k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None, t_off: int = 0,
+                  k_pe: Optional[torch.Tensor] = None, cos: Optional[torch.Tensor] = None,
+                  sin: Optional[torch.Tensor] = None, pos: Optional[torch.Tensor] = None,
+                  pairing="half", kv_dtype=torch.float16) -> Tuple[torch.Tensor, torch.Tensor]:
+    """kv_b_proj of c_norm (fp32 [B, T, R]) by W (bf16 [H*(Dn+Dv), R]).
+
+    Without k/v: returns new k_nope [B, H, T, Dn] and v [B, H, T, Dv].
+    New tensors take `kv_dtype` (bf16 or fp16); given k and v must share
+    one of those element types.
+    With k [B, H, Tcap, k_ld] and v [B, H, Tcap, Dv]: writes rows
+    t_off .. t_off+T-1; with k_pe [B, T, Dr] also writes the rotated shared
+    key into k[..., Dn:Dn+Dr] of every head (append mode)."""
+    _need(c_norm, "c_norm", torch.float32)
+    _need(W, "W")
+    B, T, R = c_norm.shape
+    if k is None:
+        k = torch.empty((B, H, T, Dn), dtype=kv_dtype, device=c_norm.device)
+    if v is None:
+        v = torch.empty((B, H, k.shape[2], Dv), dtype=k.dtype, device=c_norm.device)
+    code = _kv_code(k, "k")
+    _need(k, "k", k.dtype)
+    _need(v, "v", k.dtype)
+    _shape(W, "W", (H * (Dn + Dv), R))
+    if k.dim() != 4 or tuple(k.shape[:2]) != (B, H):
+        raise ValueError(f"k should be [B={B}, H={H}, Tcap, k_ld], but is {tuple(k.shape)}")
+    _shape(v, "v", (B, H, k.shape[2], Dv))
+    Dr = 0
+    table_len = 0
+    if k_pe is not None:
+        _need(k_pe, "k_pe")
+        _need(cos, "cos", torch.float32)
+        _need(sin, "sin", torch.float32)
+        Dr = k_pe.shape[-1]
+        _shape(k_pe, "k_pe", (B, T, Dr))
+        _shape(sin, "sin", cos.shape)
+        if cos.dim() != 2 or cos.shape[1] != Dr // 2:
+            raise ValueError(f"cos should be [table_len, {Dr // 2}], but is {tuple(cos.shape)}")
+        table_len = cos.shape[0]
+    if pos is not None:
+        _need(pos, "pos", torch.int32)
+        _shape(pos, "pos", (B, T))
+    check("mla_kv_expand",
+          _lib.load().mla_kv_expand(_ptr(c_norm), _ptr(W), B, T, R, H, Dn, Dv, _ptr(k), k.shape[-1], _ptr(v),
+                                    k.shape[2], int(t_off), code, _ptr(k_pe), _ptr(cos), _ptr(sin), table_len,
+                                    _ptr(pos), Dr, pairing_code(pairing), _stream(c_norm)))
+    return k, v
+
+
+def mla_prefill_attention(q: torch.Tensor, k_nope: torch.Tensor, k_pe: torch.Tensor, v: torch.Tensor,
+                          cos: torch.Tensor, sin: torch.Tensor, scale: float, pairing="half",
+                          pos: Optional[torch.Tensor] = None, return_lse: bool = False,
+                          out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Causal attention out [B, H, T, Dv] bf16 (and lse [B, H, T] fp32).
+
+    q [B, H, T, Dn+Dr] bf16, k_nope [B, H, T, Dn] and v [B, H, T, Dv] (both
+    bf16 or both fp16), k_pe [B, T, Dr] bf16 (not rotated), cos/sin
+    [table_len, Dr/2] fp32."""
+    for t, n in ((q, "q"), (k_pe, "k_pe")):
+        _need(t, n)
+    code = _kv_code(k_nope, "k_nope")
+    _need(k_nope, "k_nope", k_nope.dtype)
+    _need(v, "v", k_nope.dtype)
+    _need(cos, "cos", torch.float32)
+    _need(sin, "sin", torch.float32)
+    B, H, T, Dqk = q.shape
+    Dn = k_nope.shape[-1]
+    Dr = k_pe.shape[-1]
+    Dv = v.shape[-1]
+    _shape(k_nope, "k_nope", (B, H, T, Dqk - Dr))
+    _shape(k_pe, "k_pe", (B, T, Dr))
+    _shape(v, "v", (B, H, T, Dv))
+    _shape(sin, "sin", cos.shape)
+    if cos.dim() != 2 or cos.shape[1] != Dr // 2:
+        raise ValueError(f"cos should be [table_len, {Dr // 2}], but is {tuple(cos.shape)}")
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty((B, H, T, Dv), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out")
+    _shape(out, "out", (B, H, T, Dv))
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if return_lse else None
+    if pos is not None:
+        _need(pos, "pos", torch.int32)
+        _shape(pos, "pos", (B, T))
+    need = ctypes.c_size_t(0)
+    args_head = (_ptr(q), _ptr(k_nope), _ptr(k_pe), _ptr(v), code, _ptr(cos), _ptr(sin), cos.shape[0], _ptr(pos), B, H,
+                 T, Dn, Dr, Dv, float(scale), pairing_code(pairing), _ptr(out), _ptr(lse))
+    check("mla_prefill_attention", lib.mla_prefill_attention(*args_head, None, ctypes.byref(need), _stream(q)))
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty((max(need.value, 1),), dtype=torch.uint8, device=q.device)
+    have = ctypes.c_size_t(workspace.numel())
+    check("mla_prefill_attention",
+          lib.mla_prefill_attention(*args_head, _ptr(workspace), ctypes.byref(have), _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+def mla_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_len: torch.Tensor,
+                         q_pos: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor, scale: float, Dn: int,
+                         pairing="half", num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention out [B, H, 1, Dv] bf16 of q [B, H, 1, Dn+Dr] over the
+    expanded caches k_cache [B, H, Tcap, Dn+Dr], v_cache [B, H, Tcap, Dv]."""
+    _need(q, "q")
+    code = _kv_code(k_cache, "k_cache")
+    _need(k_cache, "k_cache", k_cache.dtype)
+    _need(v_cache, "v_cache", k_cache.dtype)
+    _need(seq_len, "seq_len", torch.int32)
+    _need(q_pos, "q_pos", torch.int32)
+    _need(cos, "cos", torch.float32)
+    _need(sin, "sin", torch.float32)
+    B, H, Tcap, Dqk = k_cache.shape
+    Dv = v_cache.shape[-1]
+    Dr = Dqk - Dn
+    _shape(q, "q", (B, H, 1, Dqk))
+    _shape(v_cache, "v_cache", (B, H, Tcap, Dv))
+    _shape(seq_len, "seq_len", (B,))
+    _shape(q_pos, "q_pos", (B,))
+    _shape(sin, "sin", cos.shape)
+    if cos.dim() != 2 or cos.shape[1] != Dr // 2:
+        raise ValueError(f"cos should be [table_len, {Dr // 2}], but is {tuple(cos.shape)}")
+    if out is None:
+        out = torch.empty((B, H, 1, Dv), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out")
+    _shape(out, "out", (B, H, 1, Dv))
+    lib = _lib.load()
+    head = (_ptr(q), _ptr(k_cache), _ptr(v_cache), code, _ptr(seq_len), _ptr(q_pos), _ptr(cos), _ptr(sin),
+            cos.shape[0], B, H, Tcap, Dn, Dr, Dv, float(scale), pairing_code(pairing), int(num_splits))
+    need = ctypes.c_size_t(0)
+    check("mla_decode_attention", lib.mla_decode_attention(*head, None, ctypes.byref(need), _ptr(out), _stream(q)))
+    if need.value == 0:
+        check("mla_decode_attention", lib.mla_decode_attention(*head, None, None, _ptr(out), _stream(q)))
+        return out
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty((need.value,), dtype=torch.uint8, device=q.device)
+    have = ctypes.c_size_t(workspace.numel())
+    check("mla_decode_attention",
+          lib.mla_decode_attention(*head, _ptr(workspace), ctypes.byref(have), _ptr(out), _stream(q)))
+    return out

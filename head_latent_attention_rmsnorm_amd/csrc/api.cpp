@@ -1,0 +1,236 @@
+// C ABI of the library: argument validation on the host, then the kernel
+// launchers. Every check runs before any HIP call, so a rejected call queues
+// nothing and touches no device state.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/mla.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;  // sanity bound on tensor sizes
+
+bool rope_type_ok(int32_t t) { return t == MLA_ROPE_DEFAULT || t == MLA_ROPE_YARN; }
+bool pairing_ok(int32_t p) { return p == MLA_PAIR_HALF || p == MLA_PAIR_INTERLEAVED; }
+bool dtype_ok(int32_t d) { return d == MLA_DTYPE_BF16 || d == MLA_DTYPE_FP16; }
+bool aligned16(const void* p) { return (((uintptr_t)p) & 15) == 0; }
+
+// YaRN magnitude correction (Kimi-K2 "RoPE coefficients": 1 when the scale
+// factor is at most 1, else 0.1*mscale*ln(factor) + 1).
+double yarn_mscale(double scale, double mscale) {
+  if (scale <= 1.0) return 1.0;
+  return 0.1 * mscale * log(scale) + 1.0;
+}
+
+// Correction dim of a rotation count (same page, yarn_find_correction_dim).
+double yarn_corr_dim(double nrot, int dim, double base, double max_pos) {
+  return (dim * log(max_pos / (nrot * 2.0 * M_PI))) / (2.0 * log(base));
+}
+
+mla_status check_rope(const mla_rope_params* p) {
+  if (!p) return MLA_ERR_NULL;
+  if (!rope_type_ok(p->type)) return MLA_ERR_ROPE_TYPE;
+  if (p->rope_dim < 2 || p->rope_dim > 256 || (p->rope_dim & 1)) return MLA_ERR_SHAPE;
+  if (!(p->base > 1.0) || !isfinite(p->base)) return MLA_ERR_SHAPE;
+  if (p->type == MLA_ROPE_YARN) {
+    if (!(p->factor > 0.0) || !isfinite(p->factor) || p->original_max_pos <= 0 || !(p->beta_fast > 0.0) ||
+        !(p->beta_slow > 0.0) || !isfinite(p->mscale) || !isfinite(p->mscale_all_dim))
+      return MLA_ERR_SHAPE;
+    // the mscale ratio must be finite and non-zero
+    const double den = yarn_mscale(p->factor, p->mscale_all_dim);
+    if (den == 0.0 || !isfinite(den)) return MLA_ERR_SHAPE;
+  }
+  return MLA_OK;
+}
+
+mla_status hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+// The launchers report hipGetLastError() after queueing their kernels. Clear
+// any error an earlier, unrelated runtime call left behind first, so that it
+// is not reported as a failure of this call.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "null pointer";
+    case MLA_ERR_SHAPE: return "invalid shape or size";
+    case MLA_ERR_UNSUPPORTED: return "unsupported head dimensions";
+    case MLA_ERR_ROPE_TYPE: return "unknown rotary type or pairing";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+mla_status mla_softmax_scale(const mla_rope_params* p, int32_t qk_head_dim, double* scale_out) {
+  mla_status st = check_rope(p);
+  if (st != MLA_OK) return st;
+  if (!scale_out) return MLA_ERR_NULL;
+  if (qk_head_dim < 1) return MLA_ERR_SHAPE;
+  double s = pow((double)qk_head_dim, -0.5);
+  if (p->type == MLA_ROPE_YARN && p->mscale_all_dim != 0.0) {
+    const double g = yarn_mscale(p->factor, p->mscale_all_dim);
+    s = s * g * g;
+  }
+  *scale_out = s;
+  return MLA_OK;
+}
+
+mla_status mla_rope_table_build(const mla_rope_params* p, int32_t n_pos, float* cos_out, float* sin_out,
+                                double* attn_mscale2, hipStream_t stream) {
+  mla_status st = check_rope(p);
+  if (st != MLA_OK) return st;
+  if (!cos_out || !sin_out) return MLA_ERR_NULL;
+  if (n_pos < 1 || (int64_t)n_pos * (p->rope_dim / 2) > ((int64_t)1 << 31) - 1) return MLA_ERR_SHAPE;
+  mla::RopeResolved r;
+  r.dim = p->rope_dim;
+  r.base = (float)p->base;
+  r.yarn = p->type == MLA_ROPE_YARN;
+  r.factor = (float)(r.yarn ? p->factor : 1.0);
+  r.low = 0.f;
+  r.high = 1.f;
+  r.mscale = 1.f;
+  double m2 = 1.0;
+  if (r.yarn) {
+    // correction band in double, as the page computes it with Python floats
+    double lo = floor(yarn_corr_dim(p->beta_fast, p->rope_dim, p->base, p->original_max_pos));
+    double hi = ceil(yarn_corr_dim(p->beta_slow, p->rope_dim, p->base, p->original_max_pos));
+    if (lo < 0) lo = 0;
+    if (hi > p->rope_dim - 1) hi = p->rope_dim - 1;
+    if (lo == hi) hi += 0.001;  // degenerate band
+    r.low = (float)lo;
+    r.high = (float)hi;
+    r.mscale = (float)(yarn_mscale(p->factor, p->mscale) / yarn_mscale(p->factor, p->mscale_all_dim));
+    if (p->mscale_all_dim != 0.0) {
+      const double g = yarn_mscale(p->factor, p->mscale_all_dim);
+      m2 = g * g;
+    }
+  }
+  if (attn_mscale2) *attn_mscale2 = m2;
+  clear_stale_error();
+  return hip_status(mla::launch_rope_table(r, n_pos, cos_out, sin_out, stream));
+}
+
+mla_status mla_latent_rmsnorm(const mla_bf16* x, const mla_bf16* w, float eps, float* y, int32_t n, int32_t R,
+                              hipStream_t stream) {
+  if (n < 0 || R < 1 || R > 8192 || !(eps >= 0.0f) || !isfinite(eps)) return MLA_ERR_SHAPE;
+  if ((int64_t)n * R > kMaxElems) return MLA_ERR_SHAPE;
+  if (n == 0) return MLA_OK;
+  if (!x || !w || !y) return MLA_ERR_NULL;
+  clear_stale_error();
+  return hip_status(mla::launch_rmsnorm(x, w, eps, y, n, R, stream));
+}
+
+mla_status mla_kv_expand(const float* c_norm, const mla_bf16* W, int32_t B, int32_t T, int32_t R, int32_t H,
+                         int32_t Dn, int32_t Dv, uint16_t* k, int32_t k_ld, uint16_t* v, int32_t Tcap, int32_t t_off,
+                         int32_t kv_dtype, const mla_bf16* k_pe, const float* cos, const float* sin,
+                         int32_t table_len, const int32_t* pos, int32_t Dr, int32_t pairing, hipStream_t stream) {
+  if (!dtype_ok(kv_dtype)) return MLA_ERR_UNSUPPORTED;
+  if (B < 0 || T < 0) return MLA_ERR_SHAPE;
+  if ((int64_t)B * T == 0) return MLA_OK;
+  if (!c_norm || !W || !k || !v) return MLA_ERR_NULL;
+  if (B < 0 || T < 0 || H < 1 || R < 8 || R > 4096 || (R % 8)) return MLA_ERR_SHAPE;
+  if (Dn < 8 || Dn > 512 || (Dn % 8) || Dv < 8 || Dv > 512 || (Dv % 8)) return MLA_ERR_SHAPE;
+  if (Tcap < 1 || t_off < 0 || (int64_t)t_off + T > Tcap) return MLA_ERR_SHAPE;
+  if (k_ld < Dn || (k_ld % 8)) return MLA_ERR_SHAPE;
+  if ((int64_t)B * T > ((int64_t)1 << 30) || (int64_t)H * (Dn + Dv) > ((int64_t)1 << 30)) return MLA_ERR_SHAPE;
+  if ((int64_t)B * H * Tcap * (int64_t)(k_ld > Dv ? k_ld : Dv) > kMaxElems) return MLA_ERR_SHAPE;
+  if (!aligned16(c_norm) || !aligned16(W) || !aligned16(k) || !aligned16(v)) return MLA_ERR_SHAPE;
+  const bool append = k_pe != nullptr;
+  if (append) {
+    if (!cos || !sin) return MLA_ERR_NULL;
+    if (!pairing_ok(pairing)) return MLA_ERR_ROPE_TYPE;
+    if (Dr < 2 || (Dr & 1) || Dr > 256 || k_ld < Dn + Dr || table_len < 1) return MLA_ERR_SHAPE;
+    if (!pos && t_off + T > table_len) return MLA_ERR_SHAPE;
+  }
+  mla::ExpandArgs a{c_norm, W, k, v, B, T, R, H, Dn, Dv, k_ld, Tcap, t_off, kv_dtype};
+  clear_stale_error();
+  hipError_t e = mla::launch_kv_expand(a, stream);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  if (append) {
+    mla::RotKeyArgs r{k_pe, cos, sin, table_len, pos, k, B, T, H, Dr, Tcap, t_off, k_ld, Dn, pairing, kv_dtype};
+    e = mla::launch_rotate_key(r, stream);
+  }
+  return hip_status(e);
+}
+
+static size_t prefill_ws(int32_t B, int32_t T, int32_t Dr) {
+  return (((size_t)B * T * Dr * sizeof(uint16_t)) + 255) / 256 * 256;
+}
+
+mla_status mla_prefill_attention(const mla_bf16* q, const uint16_t* k_nope, const mla_bf16* k_pe, const uint16_t* v,
+                                 int32_t kv_dtype, const float* cos, const float* sin, int32_t table_len,
+                                 const int32_t* pos,
+                                 int32_t B, int32_t H, int32_t T, int32_t Dn, int32_t Dr, int32_t Dv, float scale,
+                                 int32_t pairing, mla_bf16* out, float* lse, void* workspace, size_t* ws_bytes,
+                                 hipStream_t stream) {
+  if (B < 0 || H < 1 || T < 0 || Dn < 1 || Dr < 2 || (Dr & 1) || Dv < 1) return MLA_ERR_SHAPE;
+  if (!mla::prefill_supported(Dn + Dr, Dr, Dv) || !dtype_ok(kv_dtype)) return MLA_ERR_UNSUPPORTED;
+  if (!pairing_ok(pairing)) return MLA_ERR_ROPE_TYPE;
+  if ((int64_t)B * H * T * (Dn + Dr) > kMaxElems || (int64_t)B * H > ((int64_t)1 << 24) ||
+      (int64_t)T > ((int64_t)1 << 26))
+    return MLA_ERR_SHAPE;
+  const size_t need = prefill_ws(B, T, Dr);
+  if (!workspace && ws_bytes) {
+    *ws_bytes = need;
+    return MLA_OK;
+  }
+  if (!(scale > 0.0f) || !isfinite(scale)) return MLA_ERR_SHAPE;
+  if ((int64_t)B * T == 0) return MLA_OK;
+  if (!q || !k_nope || !k_pe || !v || !cos || !sin || !out) return MLA_ERR_NULL;
+  if (table_len < 1 || (!pos && T > table_len)) return MLA_ERR_SHAPE;
+  if (!workspace || (ws_bytes && *ws_bytes < need)) return MLA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k_nope) || !aligned16(k_pe) || !aligned16(v) || !aligned16(out) ||
+      !aligned16(workspace))
+    return MLA_ERR_SHAPE;
+  uint16_t* k_rot = static_cast<uint16_t*>(workspace);
+  clear_stale_error();
+  mla::RotKeyArgs r{k_pe, cos, sin, table_len, pos, k_rot, B, T, 1, Dr, T, 0, Dr, 0, pairing, kv_dtype};
+  hipError_t e = mla::launch_rotate_key(r, stream);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  mla::PrefillArgs a{q, k_nope, k_rot, v, cos, sin, table_len, pos, out, lse, B, H, T, Dn, Dr, Dv, pairing, scale,
+                     kv_dtype};
+  return hip_status(mla::launch_prefill(a, stream));
+}
+
+mla_status mla_decode_attention(const mla_bf16* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                int32_t cache_dtype, const int32_t* seq_len, const int32_t* q_pos, const float* cos, const float* sin,
+                                int32_t table_len, int32_t B, int32_t H, int32_t Tcap, int32_t Dn, int32_t Dr,
+                                int32_t Dv, float scale, int32_t pairing, int32_t num_splits, void* workspace,
+                                size_t* ws_bytes, mla_bf16* out, hipStream_t stream) {
+  if (B < 0 || H < 1 || Tcap < 1 || Dn < 1 || Dr < 2 || (Dr & 1) || Dv < 1) return MLA_ERR_SHAPE;
+  if (!mla::decode_supported(Dn + Dr, Dv) || !dtype_ok(cache_dtype)) return MLA_ERR_UNSUPPORTED;
+  if (!pairing_ok(pairing)) return MLA_ERR_ROPE_TYPE;
+  if (num_splits < 0 || num_splits > 256 || num_splits > Tcap) return MLA_ERR_SHAPE;
+  if ((int64_t)B * H * Tcap * (Dn + Dr) > kMaxElems || B > 65535 || H > 65535) return MLA_ERR_SHAPE;
+  const int S = num_splits ? num_splits : mla::decode_auto_splits(B, H, Tcap);
+  const size_t need = mla::decode_workspace_bytes(B, H, Dv, S);
+  if (!workspace && ws_bytes) {
+    *ws_bytes = need;
+    return MLA_OK;
+  }
+  if (!(scale > 0.0f) || !isfinite(scale)) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!q || !k_cache || !v_cache || !seq_len || !q_pos || !cos || !sin || !out) return MLA_ERR_NULL;
+  if (table_len < 1) return MLA_ERR_SHAPE;
+  if (need > 0 && (!workspace || (ws_bytes && *ws_bytes < need))) return MLA_ERR_WORKSPACE;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || (need > 0 && !aligned16(workspace))) return MLA_ERR_SHAPE;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_ml = nullptr;
+  if (need > 0) {
+    const size_t n = (size_t)B * H * S;
+    part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((n * Dv * sizeof(float)) + 255) / 256 * 256);
+  }
+  clear_stale_error();
+  mla::DecodeArgs a{q, k_cache, v_cache, seq_len, q_pos, cos, sin, table_len, B, H, Tcap, Dn, Dr, Dv, pairing, S,
+                    scale, part_o, part_ml, out, cache_dtype};
+  return hip_status(mla::launch_decode(a, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Device helpers shared by the gfx950 kernels: bf16 conversion, vector types,
+// MFMA wrappers and wavefront reductions. CDNA4 only (64-wide wavefronts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// bf16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// fp32 -> bf16 bit pattern, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  __bf16 b = (__bf16)f;  // gfx950 lowers this to v_cvt_pk_bf16_f32 (RNE)
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// Two fp32 -> packed pair of bf16 (low half = a).
+__device__ __forceinline__ uint32_t pack2bf(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// 32x32x16 bf16 MFMA, fp32 accumulate. Lane l supplies A[l%32][8*(l/32)+0..7]
+// and B[8*(l/32)+0..7][l%32]; C lane l register i holds
+// C[(i/4)*8 + (l/32)*4 + i%4][l%32].
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x32 bf16 MFMA. Lane l supplies A[l%16][8*(l/16)+0..7] and
+// B[8*(l/16)+0..7][l%16]; C lane l register i holds C[4*(l/16)+i][l%16].
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// fp16 bit pattern <-> fp32 (round to nearest even on the way down).
+__device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ uint32_t pack2h(float a, float b) {
+  f16x2 v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 16-bit element types of the intermediate key/value tensors and of the
+// attention MFMA operands. Both use the same 32x32x16 MFMA rate on gfx950;
+// fp16 carries 11 significant bits against bf16's 8 (range |x| < 65504).
+struct BF16 {
+  static constexpr int code = 0;
+  __device__ static __forceinline__ float dec(uint16_t h) { return bf2f(h); }
+  __device__ static __forceinline__ uint16_t enc(float f) { return f2bf(f); }
+  __device__ static __forceinline__ uint32_t pack2(float a, float b) { return pack2bf(a, b); }
+  // low / high element of a packed pair
+  __device__ static __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  __device__ static __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  __device__ static __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  }
+};
+
+struct F16 {
+  static constexpr int code = 1;
+  __device__ static __forceinline__ float dec(uint16_t h) { return h2f(h); }
+  __device__ static __forceinline__ uint16_t enc(float f) { return f2h(f); }
+  __device__ static __forceinline__ uint32_t pack2(float a, float b) { return pack2h(a, b); }
+  __device__ static __forceinline__ float lo(uint32_t w) { return h2f((uint16_t)(w & 0xffffu)); }
+  __device__ static __forceinline__ float hi(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
+  __device__ static __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+};
+
+}  // namespace mla

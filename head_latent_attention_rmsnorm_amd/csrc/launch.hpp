@@ -1,0 +1,95 @@
+// Host-side launchers of the gfx950 kernels. Arguments have been validated
+// by the C-ABI layer (api.cpp) before any of these is called; each launcher
+// only queues work on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Rotary table parameters resolved on the host: the correction band and the
+// mscale ratio (double on the host, handed to the device as fp32).
+struct RopeResolved {
+  int dim;
+  int yarn;
+  float base;
+  float factor;
+  float low;
+  float high;
+  float mscale;
+};
+
+hipError_t launch_rope_table(const RopeResolved& r, int n_pos, float* cos_out, float* sin_out,
+                             hipStream_t stream);
+
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* w, float eps, float* y, int n, int R,
+                          hipStream_t stream);
+
+struct ExpandArgs {
+  const float* c;     // [B*T, R] normalised latent, fp32
+  const uint16_t* W;  // [N, R], N = H*(Dn+Dv)
+  uint16_t* k;        // [B, H, Tcap, k_ld]
+  uint16_t* v;        // [B, H, Tcap, Dv]
+  int B, T, R, H, Dn, Dv, k_ld, Tcap, t_off;
+  int kv_dtype;       // element type of k and v: 0 bf16, 1 fp16
+};
+hipError_t launch_kv_expand(const ExpandArgs& a, hipStream_t stream);
+
+// Rotate the shared rotary key of every token (b, t) at pos[b*T+t] (or
+// t_off+t) and write it to dst + ((b*H + h)*Tcap + t_off + t)*ld + col for
+// every head h in [0, H) (H = 1 with Tcap = T, t_off = 0 gives a compact
+// [B, T, Dr] copy).
+struct RotKeyArgs {
+  const uint16_t* k_pe;  // [B, T, Dr]
+  const float* cos;
+  const float* sin;
+  int table_len;
+  const int32_t* pos;  // [B, T] or null
+  uint16_t* dst;
+  int B, T, H, Dr, Tcap, t_off, ld, col, pairing;
+  int dtype;  // element type of dst: 0 bf16, 1 fp16
+};
+hipError_t launch_rotate_key(const RotKeyArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+  const uint16_t* q;       // [B, H, T, Dqk]
+  const uint16_t* k_nope;  // [B, H, T, Dn]  (kv_dtype)
+  const uint16_t* k_rot;   // [B, T, Dr] rotated (workspace, kv_dtype)
+  const uint16_t* v;       // [B, H, T, Dv]  (kv_dtype)
+  const float* cos;
+  const float* sin;
+  int table_len;
+  const int32_t* pos;  // [B, T] or null
+  uint16_t* out;       // [B, H, T, Dv]
+  float* lse;          // [B, H, T] or null
+  int B, H, T, Dn, Dr, Dv, pairing;
+  float scale;
+  int kv_dtype;  // 0 bf16, 1 fp16
+};
+bool prefill_supported(int Dqk, int Dr, int Dv);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+  const uint16_t* q;        // [B, H, 1, Dqk]
+  const uint16_t* k_cache;  // [B, H, Tcap, Dqk] (cache_dtype)
+  const uint16_t* v_cache;  // [B, H, Tcap, Dv]  (cache_dtype)
+  const int32_t* seq_len;   // [B]
+  const int32_t* q_pos;     // [B]
+  const float* cos;
+  const float* sin;
+  int table_len;
+  int B, H, Tcap, Dn, Dr, Dv, pairing, num_splits;
+  float scale;
+  float* part_o;  // [B, H, S, Dv]
+  float* part_ml; // [B, H, S, 2]
+  uint16_t* out;  // [B, H, 1, Dv]
+  int cache_dtype;  // 0 bf16, 1 fp16
+};
+bool decode_supported(int Dqk, int Dv);
+int decode_auto_splits(int B, int H, int Tcap);
+size_t decode_workspace_bytes(int B, int H, int Dv, int splits);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace mla

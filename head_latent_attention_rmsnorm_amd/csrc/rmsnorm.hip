@@ -1,0 +1,100 @@
+// Latent RMSNorm (equation page "Read the equation": kv_a_layernorm of the
+// compressed latent; GLM-5 "Normalized key-value latent": default epsilon
+// 1e-6). One wavefront per row; 16-byte coalesced bf16 loads; fp32 sum of
+// squares reduced across the wavefront. The normalised latent is written in
+// fp32: kv_b_proj consumes it as an exact two-term bf16 split, so the
+// normalisation adds no bf16 rounding to the keys and values.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mla {
+
+// Rows whose width R is a multiple of 8 and at most 512*NCH: each lane keeps
+// NCH chunks of 8 elements in registers (chunk c of lane l covers columns
+// 8*(l + 64*c) .. +8).
+template <int NCH>
+__global__ void __launch_bounds__(256) rmsnorm_vec_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                                                          float eps, float* __restrict__ y, int n, int R) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
+  const int nch = R >> 3;
+  const u32x4* xr = reinterpret_cast<const u32x4*>(x + (size_t)row * R);
+  u32x4 v[NCH];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = lane + 64 * c;
+    if (ch < nch) {
+      v[c] = xr[ch];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = __uint_as_float(v[c][j] << 16);
+        const float b = __uint_as_float(v[c][j] & 0xffff0000u);
+        ss += a * a + b * b;
+      }
+    }
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)R + eps);
+  const u32x4* wr = reinterpret_cast<const u32x4*>(w);
+  f32x4* yr = reinterpret_cast<f32x4*>(y + (size_t)row * R);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = lane + 64 * c;
+    if (ch < nch) {
+      const u32x4 g = wr[ch];
+      f32x4 o0, o1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = __uint_as_float(v[c][j] << 16) * r * __uint_as_float(g[j] << 16);
+        const float b = __uint_as_float(v[c][j] & 0xffff0000u) * r * __uint_as_float(g[j] & 0xffff0000u);
+        if (j < 2) {
+          o0[2 * j] = a;
+          o0[2 * j + 1] = b;
+        } else {
+          o1[2 * j - 4] = a;
+          o1[2 * j - 3] = b;
+        }
+      }
+      yr[2 * ch] = o0;
+      yr[2 * ch + 1] = o1;
+    }
+  }
+}
+
+// Any width: two passes over the row with scalar loads.
+__global__ void __launch_bounds__(256) rmsnorm_any_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                                                          float eps, float* __restrict__ y, int n, int R) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
+  const uint16_t* xr = x + (size_t)row * R;
+  float ss = 0.f;
+  for (int i = lane; i < R; i += 64) {
+    const float a = bf2f(xr[i]);
+    ss += a * a;
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)R + eps);
+  float* yr = y + (size_t)row * R;
+  for (int i = lane; i < R; i += 64) yr[i] = bf2f(xr[i]) * r * bf2f(w[i]);
+}
+
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* w, float eps, float* y, int n, int R,
+                          hipStream_t stream) {
+  const dim3 grid((n + 3) / 4), block(256);
+  const bool aligned = ((((uintptr_t)x) | ((uintptr_t)w) | ((uintptr_t)y)) & 15) == 0;
+  if (aligned && (R % 8) == 0 && R <= 512) {
+    hipLaunchKernelGGL(rmsnorm_vec_kernel<1>, grid, block, 0, stream, x, w, eps, y, n, R);
+  } else if (aligned && (R % 8) == 0 && R <= 1024) {
+    hipLaunchKernelGGL(rmsnorm_vec_kernel<2>, grid, block, 0, stream, x, w, eps, y, n, R);
+  } else if (aligned && (R % 8) == 0 && R <= 4096) {
+    hipLaunchKernelGGL(rmsnorm_vec_kernel<8>, grid, block, 0, stream, x, w, eps, y, n, R);
+  } else {
+    hipLaunchKernelGGL(rmsnorm_any_kernel, grid, block, 0, stream, x, w, eps, y, n, R);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

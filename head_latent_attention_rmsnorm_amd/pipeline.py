@@ -1,0 +1,80 @@
+"""The whole forward path as a sequence of library calls (no arithmetic here).
+
+prefill_forward: rope table -> latent RMSNorm -> kv_b_proj expansion ->
+causal attention with the rotary step fused in (Kimi-K2 "Query content
+heads", "Join query parts"; equation page "Read the equation").
+decode_step: latent RMSNorm of the new token -> kv_b_proj expansion appended
+into the expanded cache with its rotated shared key -> split-K decode
+attention (same sections, with the expanded-cache update).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import api
+
+
+@dataclass
+class RopeTable:
+    cos: torch.Tensor
+    sin: torch.Tensor
+    scale: float  # softmax scale for the head width it was built for
+
+
+def build_table(rope: api.RopeParams, n_pos: int, qk_head_dim: int, device="cuda") -> RopeTable:
+    cos, sin, _ = api.mla_rope_table_build(rope, n_pos, device)
+    return RopeTable(cos, sin, api.mla_softmax_scale(rope, qk_head_dim))
+
+
+@dataclass
+class PrefillBuffers:
+    c_norm: torch.Tensor
+    k_nope: torch.Tensor
+    v: torch.Tensor
+    out: torch.Tensor
+    workspace: Optional[torch.Tensor] = None
+
+
+def alloc_prefill(B, T, H, R, Dn, Dr, Dv, device="cuda", kv_dtype=torch.float16) -> PrefillBuffers:
+    """Intermediate buffers; k_nope and v in `kv_dtype` (fp16 by default: same
+    size and MFMA rate as bf16 on gfx950, three more significant bits)."""
+    return PrefillBuffers(
+        c_norm=torch.empty((B, T, R), dtype=torch.float32, device=device),
+        k_nope=torch.empty((B, H, T, Dn), dtype=kv_dtype, device=device),
+        v=torch.empty((B, H, T, Dv), dtype=kv_dtype, device=device),
+        out=torch.empty((B, H, T, Dv), dtype=torch.bfloat16, device=device),
+        workspace=torch.empty((((B * T * Dr * 2) + 255) // 256 * 256,), dtype=torch.uint8, device=device),
+    )
+
+
+def prefill_forward(q, latent, k_pe, gain, W, table: RopeTable, Dn: int, Dv: int, pairing="half", eps: float = 1e-6,
+                    bufs: Optional[PrefillBuffers] = None, return_lse: bool = False, kv_dtype=torch.float16):
+    """q [B,H,T,Dn+Dr], latent [B,T,R], k_pe [B,T,Dr], gain [R], W [H*(Dn+Dv),R]
+    (all bf16 on the GPU) -> out [B,H,T,Dv] bf16."""
+    B, H, T, _ = q.shape
+    R = latent.shape[-1]
+    Dr = k_pe.shape[-1]
+    if bufs is None:
+        bufs = alloc_prefill(B, T, H, R, Dn, Dr, Dv, q.device, kv_dtype)
+    api.mla_latent_rmsnorm(latent, gain, eps, out=bufs.c_norm)
+    api.mla_kv_expand(bufs.c_norm, W, H, Dn, Dv, k=bufs.k_nope, v=bufs.v)
+    return api.mla_prefill_attention(q, bufs.k_nope, k_pe, bufs.v, table.cos, table.sin, table.scale, pairing,
+                                     return_lse=return_lse, out=bufs.out, workspace=bufs.workspace)
+
+
+def decode_step(q, latent, k_pe, gain, W, k_cache, v_cache, seq_len, q_pos, slot: int, table: RopeTable, Dn: int,
+                pairing="half", eps: float = 1e-6, num_splits: int = 0, c_norm=None, out=None, workspace=None):
+    """One decode step: the new token (q [B,H,1,Dqk], latent [B,1,R], k_pe
+    [B,1,Dr]) is normalised, expanded and appended at cache row `slot`
+    (rotated at q_pos), then attends over seq_len[b] cached rows."""
+    c_norm = api.mla_latent_rmsnorm(latent, gain, eps, out=c_norm)
+    H = k_cache.shape[1]
+    Dv = v_cache.shape[-1]
+    api.mla_kv_expand(c_norm, W, H, Dn, Dv, k=k_cache, v=v_cache, t_off=slot, k_pe=k_pe, cos=table.cos,
+                      sin=table.sin, pos=q_pos.view(-1, 1) if q_pos is not None else None, pairing=pairing)
+    return api.mla_decode_attention(q, k_cache, v_cache, seq_len, q_pos, table.cos, table.sin, table.scale, Dn,
+                                    pairing, num_splits, out=out, workspace=workspace)

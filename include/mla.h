@@ -1,0 +1,238 @@
+/*
+ * mla.h - C ABI of the MI355X (gfx950) eager multi-head latent attention
+ * forward path: latent RMSNorm -> kv_b_proj expansion -> rotary embedding
+ * (default or YaRN) -> causal scaled softmax attention, plus a decode step
+ * against an expanded per-head KV cache.
+ *
+ * Pages cited below:
+ *   [eq]        equation page "Read the equation" and its "Original context":
+ *               kv = kv_b_proj(kv_a_layernorm(compressed_kv)) viewed into
+ *               heads and split into non-rotary key and value.
+ *   [K2-query]  Kimi-K2 "Query content heads", sections "Split content
+ *               heads" and "Join query parts": query split, rotation of the
+ *               rotary parts, nope|rope concatenation, scaled scores, causal
+ *               mask, fp32 softmax, value mix, expanded-cache update.
+ *   [K2-rope]   Kimi-K2 "RoPE coefficients", section "Generate RoPE
+ *               coefficients": YaRN correction range, linear ramp, mscale
+ *               ratio, cos/sin cache, class defaults, softmax-scale rule and
+ *               the RoPE-type dispatch.
+ *   [GLM-kv]    GLM-5 "Normalized key-value latent", sections "Key-value
+ *               compression" and "KV cache": latent RMSNorm with default
+ *               epsilon 1e-6, kv_b_proj shape, expand_kv, shared rotary key
+ *               broadcast to every head, interleaved rotary variant.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE memory owned by the caller; the library
+ *     never allocates, frees or retains them and keeps no global state.
+ *   - bf16 tensors are passed as uint16_t bit patterns (bfloat16, round to
+ *     nearest even on every write). All layouts are dense row-major in the
+ *     order written in brackets, innermost dimension last.
+ *   - Calls are asynchronous on `stream` (0 = the null stream). The return
+ *     value reports argument validation (checked on the host before any
+ *     device work is queued; nothing is launched on error) and launch errors
+ *     (MLA_ERR_HIP). Faults during execution surface at the caller's
+ *     synchronisation, as with any HIP kernel.
+ *   - Positions read from device arrays are not visible to the host; a
+ *     position outside [0, table_len) is clamped to the table for memory
+ *     safety and its result is unspecified.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t mla_bf16; /* bfloat16 bit pattern */
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = -1,        /* a required pointer is NULL */
+  MLA_ERR_SHAPE = -2,       /* sizes inconsistent or out of range */
+  MLA_ERR_UNSUPPORTED = -3, /* head dimensions without a compiled kernel */
+  MLA_ERR_ROPE_TYPE = -4,   /* unknown rotary type or pairing */
+  MLA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required */
+  MLA_ERR_HIP = -6          /* a HIP launch or API call failed */
+} mla_status;
+
+/* Rotary types of the RoPE dispatch [K2-rope]: no scaling -> plain rotary
+ * embedding; "yarn" -> YaRN. Linear and dynamic-NTK scaling are named on the
+ * page without their formulas and are not provided. */
+typedef enum { MLA_ROPE_DEFAULT = 0, MLA_ROPE_YARN = 1 } mla_rope_type;
+
+/* Which elements of the rotary part form a rotated pair. HALF: pair i is
+ * (x[i], x[i + Dr/2]) (the rotate-half form matching the page's duplicated
+ * cos/sin halves, used by the Kimi-K2 call [K2-query]); INTERLEAVED: pair i
+ * is (x[2i], x[2i+1]) (GLM-5 calls an interleaved variant [GLM-kv]). Each
+ * pair (a, b) becomes (a*cos - b*sin, b*cos + a*sin); element order is
+ * unchanged. */
+typedef enum { MLA_PAIR_HALF = 0, MLA_PAIR_INTERLEAVED = 1 } mla_rope_pairing;
+
+/* Element type of the expanded keys and values (k_nope, v, the KV cache) and
+ * of the attention MFMA operands. The pages keep them in the model dtype
+ * (bf16). FP16 has the same size and MFMA rate on gfx950 and three more
+ * significant bits, which keeps the whole path inside its error budget; it
+ * requires |values| < 65504 (larger ones overflow to inf). Queries, rotary
+ * keys and outputs stay bf16 at the boundary in both modes. */
+typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP16 = 1 } mla_dtype;
+
+/* Rotary parameters [K2-rope, YaRN class and rope_scaling keys]. The YaRN
+ * class defaults printed on the page are base 10000, factor 1.0,
+ * original_max_pos 4096, beta_fast 32, beta_slow 1, mscale 1,
+ * mscale_all_dim 0. Fields other than rope_dim and base are ignored for
+ * MLA_ROPE_DEFAULT. */
+typedef struct {
+  int32_t rope_dim;         /* Dr: rotary width, even, 2..256 */
+  int32_t type;             /* mla_rope_type */
+  double base;              /* rope_theta, > 1 */
+  double factor;            /* YaRN scaling factor (> 0) */
+  int32_t original_max_pos; /* YaRN original_max_position_embeddings (> 0) */
+  double beta_fast;         /* YaRN beta_fast (> 0) */
+  double beta_slow;         /* YaRN beta_slow (> 0) */
+  double mscale;            /* YaRN mscale */
+  double mscale_all_dim;    /* YaRN mscale_all_dim */
+} mla_rope_params;
+
+/* Build the cos/sin table [K2-rope, _set_cos_sin_cache].
+ *   inv_freq_i = base^(-2i/Dr) for default RoPE; for YaRN, the blend of
+ *   base^(-2i/Dr) (below the correction band) and base^(-2i/Dr)/factor (above
+ *   it) by the linear ramp over [low, high], where low/high are the floor and
+ *   ceiling of the correction dims of beta_fast/beta_slow clamped to
+ *   [0, Dr-1] (widened by 0.001 when equal).
+ *   m = mscale(factor, mscale) / mscale(factor, mscale_all_dim) for YaRN
+ *   (mscale(s, u) = 1 if s <= 1 else 0.1*u*ln(s) + 1), 1 for default.
+ *   cos_out[p, i] = m*cos(p*inv_freq_i), sin_out[p, i] = m*sin(p*inv_freq_i)
+ *   for p in [0, n_pos), i in [0, Dr/2).
+ * The correction range is computed on the host in double (as the page does
+ * with Python floats); ramp, frequencies, angles and sin/cos in fp32 on the
+ * device. The page's duplicated second half (cat(freqs, freqs)) is not
+ * stored.
+ * Args: p (host), n_pos >= 1, cos_out/sin_out device fp32 [n_pos, Dr/2].
+ *   attn_mscale2 (host, may be NULL) receives mscale(factor, mscale_all_dim)^2
+ *   if YaRN and mscale_all_dim != 0, else 1: the softmax-scale multiplier.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE (n_pos < 1, Dr odd/out of range, bad
+ *   YaRN numbers), MLA_ERR_ROPE_TYPE (unknown type), MLA_ERR_HIP. */
+mla_status mla_rope_table_build(const mla_rope_params* p, int32_t n_pos, float* cos_out,
+                                float* sin_out, double* attn_mscale2, hipStream_t stream);
+
+/* Softmax scale rule (host only, no device work) [K2-rope model-args text;
+ * GLM-kv yarn_apply_mscale]: qk_head_dim^-0.5, times
+ * mscale(factor, mscale_all_dim)^2 when the rotary type is YaRN and
+ * mscale_all_dim != 0. Errors: MLA_ERR_NULL, MLA_ERR_SHAPE
+ * (qk_head_dim < 1), MLA_ERR_ROPE_TYPE. */
+mla_status mla_softmax_scale(const mla_rope_params* p, int32_t qk_head_dim, double* scale_out);
+
+/* Latent RMSNorm [eq; GLM-kv: kv_a_layernorm built without epsilon, i.e.
+ * 1e-6]: y[r, :] = w * x[r, :] / sqrt(mean(x[r, :]^2) + eps), computed and
+ * written in fp32. The normalised latent is kept in fp32 because kv_b_proj
+ * consumes it exactly (see mla_kv_expand): rounding it to bf16 would be the
+ * largest single error of the whole path.
+ * Args: x device bf16 [n, R]; w device bf16 [R]; eps >= 0; y device fp32
+ *   [n, R]; n >= 0 rows (0 is a no-op); 1 <= R <= 8192.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_HIP. */
+mla_status mla_latent_rmsnorm(const mla_bf16* x, const mla_bf16* w, float eps, float* y, int32_t n,
+                              int32_t R, hipStream_t stream);
+
+/* kv_b_proj up-projection and head split [eq; GLM-kv expand_kv]:
+ *   kv[b, t, :] = c_norm[b, t, :] . W^T, viewed [H, Dn+Dv]; for each head h
+ *   k[b, h, t_off + t, 0:Dn]  = kv[b, t, h*(Dn+Dv) + 0 .. Dn)
+ *   v[b, h, t_off + t, 0:Dv]  = kv[b, t, h*(Dn+Dv) + Dn .. Dn+Dv)
+ * bf16 MFMA with fp32 accumulation, one RNE rounding per output to kv_dtype.
+ * The fp32 latent enters the MFMA as two bf16 terms, hi = bf16(c) and
+ * lo = bf16(c - hi), which carry it to 16 significant bits.
+ * Append mode (k_pe != NULL), the expanded-cache update of a decode step
+ * [K2-query]: additionally the shared rotary key of token (b, t) is rotated
+ * at position pos[b*T + t] (or t_off + t when pos is NULL) with the table
+ * and written to k[b, h, t_off + t, Dn : Dn+Dr] for every head h.
+ * Args: c_norm device fp32 [B, T, R] (from mla_latent_rmsnorm); W device
+ *   bf16 [H*(Dn+Dv), R]
+ *   (nn.Linear weight layout); k device [B, H, Tcap, k_ld] and v device
+ *   [B, H, Tcap, Dv], both of element type kv_dtype (mla_dtype);
+ *   0 <= t_off, t_off + T <= Tcap;
+ *   k_ld >= Dn (>= Dn+Dr in append mode). Append mode only: k_pe device bf16
+ *   [B, T, Dr] (not rotated), cos/sin device fp32 [table_len, Dr/2] from
+ *   mla_rope_table_build, pos device int32 [B, T] or NULL, pairing.
+ *   Dn, Dv multiples of 8 in [8, 512]; R multiple of 8 in [8, 4096];
+ *   B*T == 0 is a no-op.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_ROPE_TYPE (pairing),
+ *   MLA_ERR_UNSUPPORTED (kv_dtype), MLA_ERR_HIP. */
+mla_status mla_kv_expand(const float* c_norm, const mla_bf16* W, int32_t B, int32_t T,
+                         int32_t R, int32_t H, int32_t Dn, int32_t Dv, uint16_t* k, int32_t k_ld,
+                         uint16_t* v, int32_t Tcap, int32_t t_off, int32_t kv_dtype,
+                         const mla_bf16* k_pe, const float* cos, const float* sin,
+                         int32_t table_len, const int32_t* pos, int32_t Dr, int32_t pairing,
+                         hipStream_t stream);
+
+/* Causal prefill attention with the rotary step and nope|rope concatenation
+ * fused in [K2-query, Join query parts; GLM-kv expand_kv]:
+ *   Q[b,h,t]  = [ q[b,h,t,0:Dn] | rot(q[b,h,t,Dn:Dn+Dr], pos[b,t]) ]
+ *   K[b,h,s]  = [ k_nope[b,h,s,:] | rot(k_pe[b,s,:], pos[b,s]) ]  (one rotary
+ *               key shared by all heads)
+ *   S = scale * Q K^T, keys s > t hidden (causal), P = softmax over s in fp32,
+ *   out[b,h,t,:] = P V.
+ * Flash-style: S and P are never written to memory. Both products run on
+ * 16-bit MFMA in kv_dtype with fp32 accumulation: the rotated query and key
+ * parts and P are rounded once to kv_dtype.
+ * Args: q device bf16 [B, H, T, Dn+Dr] (rotary part not rotated);
+ *   k_nope device [B, H, T, Dn] and v device [B, H, T, Dv] of element type
+ *   kv_dtype (from mla_kv_expand); k_pe device bf16 [B, T, Dr] (not
+ *   rotated); cos/sin device fp32
+ *   [table_len, Dr/2]; pos device int32 [B, T] or NULL (= 0..T-1, which
+ *   needs table_len >= T); scale from mla_softmax_scale; out device bf16
+ *   [B, H, T, Dv]; lse device fp32 [B, H, T] or NULL (natural-log
+ *   log-sum-exp of each row's scaled scores).
+ *   workspace: device scratch of *ws_bytes bytes. Pass workspace == NULL with
+ *   ws_bytes != NULL to query the size (*ws_bytes is set, MLA_OK, nothing
+ *   launched).
+ *   Supported (Dn+Dr, Dv): (48, 32), (192, 128), (256, 256); Dr in
+ *   {16, 64}; T >= 0 (0 is a no-op).
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED,
+ *   MLA_ERR_ROPE_TYPE, MLA_ERR_WORKSPACE, MLA_ERR_HIP. */
+mla_status mla_prefill_attention(const mla_bf16* q, const uint16_t* k_nope, const mla_bf16* k_pe,
+                                 const uint16_t* v, int32_t kv_dtype, const float* cos,
+                                 const float* sin, int32_t table_len, const int32_t* pos,
+                                 int32_t B, int32_t H,
+                                 int32_t T, int32_t Dn, int32_t Dr, int32_t Dv, float scale,
+                                 int32_t pairing, mla_bf16* out, float* lse, void* workspace,
+                                 size_t* ws_bytes, hipStream_t stream);
+
+/* Decode attention of one new token per sequence against an expanded cache
+ * [K2-query: expanded cache update then scaled, masked softmax attention]:
+ *   Q[b,h] = [ q[b,h,0,0:Dn] | rot(q[b,h,0,Dn:], q_pos[b]) ]
+ *   S[s] = scale * Q . k_cache[b,h,s,:] for s < seq_len[b] (the cache's
+ *   rotary part is already rotated), P = softmax, out[b,h,0,:] = P V.
+ * Split-K: the seq_len[b] rows are cut into num_splits ranges, each giving a
+ * partial (max, sum, unnormalised output); a combine kernel merges them with
+ * the log-sum-exp rule. The append of the new token is a separate
+ * mla_kv_expand call in append mode before this one.
+ * Args: q device bf16 [B, H, 1, Dn+Dr]; k_cache device [B, H, Tcap, Dn+Dr]
+ *   and v_cache device [B, H, Tcap, Dv] of element type cache_dtype
+ *   (mla_dtype); seq_len
+ *   device int32 [B] (values clamped to [1, Tcap]); q_pos device int32 [B];
+ *   cos/sin device fp32 [table_len, Dr/2]; num_splits 0 = automatic, else
+ *   1..256; out device bf16 [B, H, 1, Dv]. workspace/ws_bytes as for
+ *   mla_prefill_attention (size depends on B, H, Tcap, Dv and num_splits).
+ *   Dn+Dr, Dv multiples of 8, Dn+Dr <= 512, Dv <= 512.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED,
+ *   MLA_ERR_ROPE_TYPE, MLA_ERR_WORKSPACE, MLA_ERR_HIP. */
+mla_status mla_decode_attention(const mla_bf16* q, const uint16_t* k_cache,
+                                const uint16_t* v_cache, int32_t cache_dtype, const int32_t* seq_len,
+                                const int32_t* q_pos, const float* cos, const float* sin,
+                                int32_t table_len, int32_t B, int32_t H, int32_t Tcap, int32_t Dn,
+                                int32_t Dr, int32_t Dv, float scale, int32_t pairing,
+                                int32_t num_splits, void* workspace, size_t* ws_bytes,
+                                mla_bf16* out, hipStream_t stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* mla_status_string(mla_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

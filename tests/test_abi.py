@@ -1,0 +1,156 @@
+"""C-ABI checks that need no GPU: libmla.so loads, exports every function
+include/mla.h declares, and rejects invalid arguments with the documented
+status codes before any device call (every call here fails validation, so no
+HIP work is queued)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from head_latent_attention_rmsnorm_amd import _lib
+from head_latent_attention_rmsnorm_amd._lib import RopeParams
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+OK, NULL, SHAPE, UNSUP, ROPE, WS = 0, -1, -2, -3, -4, -5
+FAKE = 0x100000  # a non-null, 16-byte-aligned address that is never dereferenced
+
+
+def declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:mla_status|const char\*)\s+(mla_\w+)\s*\(", txt, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared()
+    assert len(names) == 7
+    assert sorted(_lib.EXPORTS) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert lib.mla_status_string(code)
+    assert lib.mla_status_string(12345) == b"unknown status"
+
+
+def yarn(**kw):
+    p = dict(rope_dim=64, type=1, base=50000.0, factor=32.0, original_max_pos=4096, beta_fast=32.0, beta_slow=1.0,
+             mscale=1.0, mscale_all_dim=1.0)
+    p.update(kw)
+    return RopeParams(**p)
+
+
+def test_softmax_scale_host_rule(lib):
+    out = ctypes.c_double()
+    assert lib.mla_softmax_scale(ctypes.byref(yarn()), 192, ctypes.byref(out)) == OK
+    assert out.value == pytest.approx(0.13086079996295005, rel=1e-15)
+    assert lib.mla_softmax_scale(ctypes.byref(yarn(type=0)), 256, ctypes.byref(out)) == OK
+    assert out.value == 0.0625
+    assert lib.mla_softmax_scale(ctypes.byref(yarn(type=7)), 192, ctypes.byref(out)) == ROPE
+    assert lib.mla_softmax_scale(None, 192, ctypes.byref(out)) == NULL
+    assert lib.mla_softmax_scale(ctypes.byref(yarn()), 0, ctypes.byref(out)) == SHAPE
+
+
+def test_rope_table_validation(lib):
+    p = ctypes.byref(yarn())
+    m2 = ctypes.c_double()
+    assert lib.mla_rope_table_build(None, 10, FAKE, FAKE, None, None) == NULL
+    assert lib.mla_rope_table_build(p, 10, None, FAKE, None, None) == NULL
+    assert lib.mla_rope_table_build(p, 0, FAKE, FAKE, None, None) == SHAPE
+    assert lib.mla_rope_table_build(ctypes.byref(yarn(type=2)), 10, FAKE, FAKE, None, None) == ROPE
+    assert lib.mla_rope_table_build(ctypes.byref(yarn(rope_dim=63)), 10, FAKE, FAKE, None, None) == SHAPE
+    assert lib.mla_rope_table_build(ctypes.byref(yarn(base=1.0)), 10, FAKE, FAKE, None, None) == SHAPE
+    assert lib.mla_rope_table_build(ctypes.byref(yarn(factor=-1.0)), 10, FAKE, FAKE, ctypes.byref(m2), None) == SHAPE
+
+
+def test_rmsnorm_validation(lib):
+    assert lib.mla_latent_rmsnorm(None, FAKE, 1e-6, FAKE, 4, 512, None) == NULL
+    assert lib.mla_latent_rmsnorm(FAKE, FAKE, 1e-6, FAKE, -1, 512, None) == SHAPE
+    assert lib.mla_latent_rmsnorm(FAKE, FAKE, 1e-6, FAKE, 4, 0, None) == SHAPE
+    assert lib.mla_latent_rmsnorm(FAKE, FAKE, -1.0, FAKE, 4, 512, None) == SHAPE
+    assert lib.mla_latent_rmsnorm(FAKE, FAKE, float("nan"), FAKE, 4, 512, None) == SHAPE
+    assert lib.mla_latent_rmsnorm(FAKE, FAKE, 1e-6, FAKE, 0, 512, None) == OK  # empty: no-op
+    assert lib.mla_latent_rmsnorm(None, None, 1e-6, None, 0, 512, None) == OK
+
+
+def expand(lib, **kw):
+    a = dict(c=FAKE, W=FAKE, B=1, T=4, R=512, H=2, Dn=128, Dv=128, k=FAKE, k_ld=128, v=FAKE, Tcap=4, t_off=0,
+             kv_dtype=1, k_pe=None, cos=None, sin=None, table_len=0, pos=None, Dr=0, pairing=0)
+    a.update(kw)
+    return lib.mla_kv_expand(*a.values(), None)
+
+
+def test_kv_expand_validation(lib):
+    assert expand(lib, c=None) == NULL
+    assert expand(lib, R=500) == SHAPE  # not a multiple of 8
+    assert expand(lib, Dn=100) == SHAPE
+    assert expand(lib, t_off=1) == SHAPE  # t_off + T > Tcap
+    assert expand(lib, k_ld=64) == SHAPE
+    assert expand(lib, c=FAKE + 2) == SHAPE  # misaligned
+    # append mode needs the table and a wide enough key row
+    assert expand(lib, k_pe=FAKE, Dr=64, k_ld=192) == NULL
+    assert expand(lib, k_pe=FAKE, cos=FAKE, sin=FAKE, table_len=4, Dr=64, k_ld=128) == SHAPE
+    assert expand(lib, k_pe=FAKE, cos=FAKE, sin=FAKE, table_len=4, Dr=64, k_ld=192, pairing=5) == ROPE
+    assert expand(lib, k_pe=FAKE, cos=FAKE, sin=FAKE, table_len=2, Dr=64, k_ld=192) == SHAPE  # table too short
+    assert expand(lib, kv_dtype=2) == UNSUP
+    assert expand(lib, B=0) == OK  # empty: no-op
+    assert expand(lib, T=0, c=None, k=None) == OK  # empty tensors may have null data
+
+
+def prefill(lib, ws=FAKE, ws_bytes=None, **kw):
+    a = dict(q=FAKE, kn=FAKE, kpe=FAKE, v=FAKE, kv_dtype=1, cos=FAKE, sin=FAKE, table_len=4096, pos=None, B=1, H=64,
+             T=4096, Dn=128, Dr=64, Dv=128, scale=0.13, pairing=0, out=FAKE, lse=None)
+    a.update(kw)
+    return lib.mla_prefill_attention(*a.values(), ws, ws_bytes, None)
+
+
+def test_prefill_validation(lib):
+    need = ctypes.c_size_t(0)
+    assert prefill(lib, ws=None, ws_bytes=ctypes.byref(need)) == OK
+    assert need.value == 4096 * 64 * 2
+    assert prefill(lib, q=None) == NULL
+    assert prefill(lib, Dn=100) == UNSUP
+    assert prefill(lib, Dv=64) == UNSUP
+    assert prefill(lib, pairing=3) == ROPE
+    assert prefill(lib, scale=0.0) == SHAPE
+    assert prefill(lib, table_len=100) == SHAPE  # implicit positions 0..T-1 exceed the table
+    assert prefill(lib, ws=None) == WS
+    small = ctypes.c_size_t(16)
+    assert prefill(lib, ws_bytes=ctypes.byref(small)) == WS
+    assert prefill(lib, kv_dtype=-1) == UNSUP
+    assert prefill(lib, T=0) == OK  # empty: no-op
+    assert prefill(lib, T=0, q=None, out=None) == OK
+    assert prefill(lib, T=-1) == SHAPE
+
+
+def decode(lib, ws=FAKE, ws_bytes=None, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, dtype=0, seq=FAKE, qpos=FAKE, cos=FAKE, sin=FAKE, table_len=1001, B=32,
+             H=64, Tcap=1001, Dn=128, Dr=64, Dv=128, scale=0.13, pairing=0, splits=4)
+    a.update(kw)
+    return lib.mla_decode_attention(*a.values(), ws, ws_bytes, FAKE, None)
+
+
+def test_decode_validation(lib):
+    need = ctypes.c_size_t(0)
+    assert decode(lib, ws=None, ws_bytes=ctypes.byref(need)) == OK
+    assert need.value >= 32 * 64 * 4 * (128 + 2) * 4
+    assert decode(lib, splits=1, ws=None, ws_bytes=ctypes.byref(need)) == OK
+    assert need.value == 0
+    assert decode(lib, kc=None) == NULL
+    assert decode(lib, Dn=96) == UNSUP
+    assert decode(lib, pairing=-1) == ROPE
+    assert decode(lib, splits=-2) == SHAPE
+    assert decode(lib, splits=300) == SHAPE
+    assert decode(lib, ws=None) == WS
+    assert decode(lib, dtype=3) == UNSUP
+    assert decode(lib, B=0) == OK

@@ -1,0 +1,347 @@
+"""GPU parity: every C-ABI entry point against the fp64 oracle on the same
+seeded inputs, staged (table, RMSNorm, expansion, attention alone) and end to
+end, on the five workloads and on ragged / edge shapes."""
+
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import mla_oracle as O
+from tests.gpu_util import BF16_MAX_ABS, MAX_ABS, REL_L2, assert_close, errors, f64, head_view, say, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+M = pytest.importorskip("head_latent_attention_rmsnorm_amd")
+api, pipeline = M.api, M.pipeline
+W_ = workloads.WORKLOADS
+
+
+def table(w, n_pos=None):
+    return pipeline.build_table(api.params_from(w.rope, w.Dr), n_pos or max(w.table_len, 1), w.Dqk)
+
+
+# --------------------------------------------------------------------- table
+
+TABLE_SPECS = [
+    ("kimi_yarn", workloads.YARN_KIMI, 64, 8192),
+    ("default_1e4", workloads.RopeSpec(kind="default", base=10000.0), 64, 4096),
+    ("tiny", workloads.RopeSpec(kind="default", base=10000.0), 16, 32),
+    ("yarn_class_defaults", workloads.RopeSpec(kind="yarn", base=10000.0, factor=40.0, original_max_pos=4096,
+                                               beta_fast=32.0, beta_slow=1.0, mscale=1.0, mscale_all_dim=0.0), 64, 3000),
+    ("yarn_degenerate_band", workloads.RopeSpec(kind="yarn", base=10000.0, factor=4.0, original_max_pos=64,
+                                                beta_fast=2.0, beta_slow=2.0, mscale=0.8, mscale_all_dim=0.5), 8, 100),
+]
+
+
+@pytest.mark.parametrize("name,spec,dim,n", TABLE_SPECS, ids=[t[0] for t in TABLE_SPECS])
+def test_rope_table(name, spec, dim, n):
+    say(f"[table] {name} dim={dim} n_pos={n}")
+    cos, sin, m2 = api.mla_rope_table_build(api.params_from(spec, dim), n)
+    torch.cuda.synchronize()
+    rc, rs = O.rope_table(spec, dim, n)
+    m = O.rope_table_mscale(spec)
+    ang = np.arange(n)[:, None] * O.rope_inv_freq(spec, dim)[None, :]
+    # fp32 frequencies and angles: relative error of a few ulp in the angle,
+    # plus the rounding of sin/cos and of the mscale product
+    tol = abs(m) * (ang * 4e-7 + 1e-6)
+    for got, ref, what in ((cos, rc, "cos"), (sin, rs, "sin")):
+        d = np.abs(f64(got) - ref)
+        say(f"  {what}: max err {d.max():.3e}, max err/tol {(d / tol).max():.3f}")
+        assert np.all(d <= tol), what
+    s = O.softmax_scale(spec, 192)
+    assert m2 == pytest.approx(s * math.sqrt(192) if spec.kind == "yarn" and spec.mscale_all_dim else 1.0, rel=1e-12)
+
+
+# --------------------------------------------------------------------- RMSNorm
+
+@pytest.mark.parametrize("n,R", [(4096, 512), (7, 512), (33, 64), (5, 1000), (3, 2048), (9, 100), (1, 8)])
+def test_rmsnorm(n, R):
+    say(f"[rmsnorm] n={n} R={R}")
+    g = torch.Generator().manual_seed(n * 1000 + R)
+    x = (torch.randn(n, R, generator=g) * 3).to(torch.bfloat16)
+    w = (1 + 0.3 * torch.randn(R, generator=g)).to(torch.bfloat16)
+    y = api.mla_latent_rmsnorm(x.cuda(), w.cuda(), 1e-6)
+    ref = O.rmsnorm(f64(x), f64(w), 1e-6)
+    d = np.abs(f64(y) - ref)
+    # fp32 throughout: the sum of R squares (relative error <= R u), its
+    # root (half of that), the reciprocal and two products (a few u)
+    u = 2.0 ** -24
+    assert np.all(d <= np.abs(ref) * (R * u + 8 * u)), (d / np.abs(ref)).max()
+
+
+# --------------------------------------------------------------------- kv_b_proj
+
+EXPAND_SHAPES = [
+    dict(B=1, T=1024, H=64, R=512, Dn=128, Dv=128),
+    dict(B=2, T=150, H=3, R=64, Dn=32, Dv=32),        # ragged tokens and columns
+    dict(B=1, T=513, H=4, R=512, Dn=192, Dv=256),     # GLM-5 head widths
+    dict(B=3, T=1, H=5, R=104, Dn=8, Dv=24),          # reduction not a multiple of the stage
+]
+
+
+# one RNE rounding of the fp32 product (half an ulp) plus the fp32
+# accumulation and the 16-bit latent split (far below an ulp)
+EXPAND_REL = {torch.float16: 2.0 ** -11 * 1.01, torch.bfloat16: 2.0 ** -8 * 1.01}
+
+
+@pytest.mark.parametrize("kv_dtype", [torch.float16, torch.bfloat16], ids=["fp16", "bf16"])
+@pytest.mark.parametrize("s", EXPAND_SHAPES, ids=lambda s: "B{B}T{T}H{H}R{R}n{Dn}v{Dv}".format(**s))
+def test_kv_expand(s, kv_dtype):
+    say(f"[kv_expand] {s} {kv_dtype}")
+    g = torch.Generator().manual_seed(s["T"] * 7 + s["H"])
+    c = torch.randn(s["B"], s["T"], s["R"], generator=g)
+    Wt = (torch.randn(s["H"] * (s["Dn"] + s["Dv"]), s["R"], generator=g) / math.sqrt(s["R"])).to(torch.bfloat16)
+    k, v = api.mla_kv_expand(c.cuda(), Wt.cuda(), s["H"], s["Dn"], s["Dv"], kv_dtype=kv_dtype)
+    assert k.dtype == kv_dtype and v.dtype == kv_dtype
+    rk, rv = O.kv_expand(f64(c), f64(Wt), s["H"], s["Dn"], s["Dv"])
+    for got, ref, what in ((k, rk, "k_nope"), (v, rv, "v")):
+        d = np.abs(f64(got) - ref)
+        bound = np.abs(ref) * EXPAND_REL[kv_dtype] + 2.0 ** -20
+        say(f"  {what}: max err {d.max():.3e}, max err/bound {(d / bound).max():.3f}")
+        assert np.all(d <= bound), what
+
+
+def test_kv_expand_append_into_cache():
+    say("[kv_expand append]")
+    w = W_["kimi_k2_decode"]
+    B, H, Tcap, slot = 4, 6, 40, 29
+    g = torch.Generator().manual_seed(9)
+    c = torch.randn(B, 2, w.R, generator=g)
+    Wt = (torch.randn(H * (w.Dn + w.Dv), w.R, generator=g) / math.sqrt(w.R)).to(torch.bfloat16)
+    kpe = torch.randn(B, 2, w.Dr, generator=g).to(torch.bfloat16)
+    kc = torch.full((B, H, Tcap, w.Dqk), 7.0, dtype=torch.bfloat16).cuda()
+    vc = torch.full((B, H, Tcap, w.Dv), -3.0, dtype=torch.bfloat16).cuda()
+    tab = table(w, Tcap)
+    pos = torch.tensor([[slot, slot + 1]] * B, dtype=torch.int32)
+    api.mla_kv_expand(c.cuda(), Wt.cuda(), H, w.Dn, w.Dv, k=kc, v=vc, t_off=slot, k_pe=kpe.cuda(), cos=tab.cos,
+                      sin=tab.sin, pos=pos.cuda(), pairing="half")
+    kc, vc = kc.cpu(), vc.cpu()
+    rk, rv = O.kv_expand(f64(c), f64(Wt), H, w.Dn, w.Dv)
+    cos, sin = O.rope_table(w.rope, w.Dr, Tcap)
+    rpe = O.rotate(f64(kpe), cos[slot:slot + 2][None], sin[slot:slot + 2][None], "half")
+    got_k = f64(kc[:, :, slot:slot + 2])
+    assert np.all(np.abs(got_k[..., :w.Dn] - rk) <= np.abs(rk) * 2.0 ** -8 + 2.0 ** -14)
+    assert np.all(np.abs(f64(vc[:, :, slot:slot + 2]) - rv) <= np.abs(rv) * 2.0 ** -8 + 2.0 ** -14)
+    for h in range(H):
+        assert np.all(np.abs(got_k[:, h, :, w.Dn:] - rpe) <= np.abs(rpe) * 2.0 ** -8 + 1e-3)
+    # every other row untouched
+    mask = torch.ones(Tcap, dtype=torch.bool)
+    mask[slot:slot + 2] = False
+    assert torch.all(kc[:, :, mask] == 7.0) and torch.all(vc[:, :, mask] == -3.0)
+
+
+# --------------------------------------------------------------------- prefill
+
+def run_prefill(w, inp, return_lse=False, kv_dtype=torch.float16):
+    g = to_gpu(inp)
+    tab = table(w)
+    res = pipeline.prefill_forward(g["q"], g["latent"], g["k_pe"], g["gain"], g["W"], tab, w.Dn, w.Dv, w.pairing,
+                                   w.eps, return_lse=return_lse, kv_dtype=kv_dtype)
+    torch.cuda.synchronize()
+    return res
+
+
+def staged_attention_check(w, inp, heads, rows=None, kv_dtype=torch.float16):
+    """Attention alone: the oracle's attention fed the GPU's own 16-bit
+    k_nope/v (isolates the attention kernel from the expansion's rounding)."""
+    g = to_gpu(inp)
+    tab = table(w)
+    c = api.mla_latent_rmsnorm(g["latent"], g["gain"], w.eps)
+    kn, v = api.mla_kv_expand(c, g["W"], w.H, w.Dn, w.Dv, kv_dtype=kv_dtype)
+    out = api.mla_prefill_attention(g["q"], kn, g["k_pe"], v, tab.cos, tab.sin, tab.scale, w.pairing)
+    torch.cuda.synchronize()
+    cos, sin = O.rope_table(w.rope, w.Dr, w.T)
+    qf = f64(inp["q"])
+    q_pe = O.rotate(qf[..., w.Dn:], cos[None, None], sin[None, None], w.pairing)
+    k_pe = O.rotate(f64(inp["k_pe"]), cos[None], sin[None], w.pairing)
+    pos = np.arange(w.T)
+    rows = pos if rows is None else np.asarray(rows)
+    for (b, h) in heads:
+        Q = np.concatenate([qf[b, h, :, :w.Dn], q_pe[b, h]], -1)
+        K = np.concatenate([f64(kn[b, h]), k_pe[b]], -1)
+        ref = O.attention(Q[rows], K, f64(v[b, h]), O.softmax_scale(w.rope, w.Dqk), rows, pos)
+        assert_close(f64(out[b, h])[rows], ref, f"attention-only b={b} h={h} {kv_dtype}",
+                     max_abs=MAX_ABS if kv_dtype == torch.float16 else BF16_MAX_ABS)
+
+
+@pytest.mark.parametrize("name", ["tiny", "kimi_k2_1k"])
+def test_prefill_full(name):
+    w = W_[name]
+    say(f"[prefill full] {name}")
+    inp = workloads.make_inputs(w)
+    out, lse = run_prefill(w, inp, return_lse=True)
+    parts = O.prefill_parts(w, inp)
+    ref = np.empty((w.B, w.H, w.T, w.Dv))
+    ref_lse = np.empty((w.B, w.H, w.T))
+    for b in range(w.B):
+        for h in range(w.H):
+            ref[b, h], ref_lse[b, h] = O.prefill_head(w, parts, b, h, return_lse=True)
+    assert_close(f64(out), ref, f"{name} output")
+    ma, _ = errors(f64(lse), ref_lse)
+    say(f"  lse max_abs={ma:.3e}")
+    assert ma < 2e-2
+    staged_attention_check(w, inp, [(0, 0), (0, w.H - 1)])
+
+
+def test_prefill_glm5_sampled_heads():
+    w = W_["glm5_4k"]
+    say("[prefill] glm5_4k, 6 heads against the oracle")
+    inp = workloads.make_inputs(w)
+    out = run_prefill(w, inp).cpu()
+    for h in (0, 1, 17, 40, 62, 63):
+        wh, sub = head_view(w, inp, h)
+        parts = O.prefill_parts(wh, sub)
+        ref = O.prefill_head(wh, parts, 0, 0)
+        assert_close(f64(out[0, h]), ref, f"glm5 head {h}")
+    staged_attention_check(w, inp, [(0, 5)], rows=np.r_[0:64, 2000:2100, 4032:4096])
+
+
+def test_prefill_kimi_8k_sampled():
+    w = W_["kimi_k2_8k"]
+    say("[prefill] kimi_k2_8k (B=2, T=8192), sampled heads and rows")
+    inp = workloads.make_inputs(w)
+    out = run_prefill(w, inp).cpu()
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.r_[0:128, 8192 - 128:8192, rng.integers(0, 8192, 256)])
+    for (b, h) in ((0, 0), (1, 63), (1, 17), (0, 44)):
+        wh, sub = head_view(w, {k: v[b:b + 1] if k in ("q", "latent", "k_pe") else v for k, v in inp.items()}, h)
+        wh = dataclasses.replace(wh, B=1)
+        parts = O.prefill_parts(wh, sub)
+        ref = O.prefill_head(wh, parts, 0, 0, rows=rows)
+        assert_close(f64(out[b, h])[rows], ref, f"kimi 8k b={b} h={h} ({len(rows)} rows)")
+
+
+RAGGED = [
+    workloads.custom(name="k2-ragged", B=2, T=300, H=3, R=512, Dn=128, Dr=64, Dv=128, seed=31, rope=workloads.YARN_KIMI),
+    workloads.custom(name="k2-one-token", B=2, T=1, H=2, R=512, Dn=128, Dr=64, Dv=128, seed=32, rope=workloads.YARN_KIMI),
+    workloads.custom(name="glm-ragged", B=3, T=129, H=2, R=512, Dn=192, Dr=64, Dv=256, seed=33, pairing="interleaved"),
+    workloads.custom(name="tiny-ragged", B=2, T=200, H=3, R=64, Dn=32, Dr=16, Dv=32, seed=34),
+    workloads.custom(name="k2-interleaved", B=1, T=191, H=2, R=512, Dn=128, Dr=64, Dv=128, seed=35,
+                     pairing="interleaved", rope=workloads.YARN_KIMI),
+]
+
+
+@pytest.mark.parametrize("kv_dtype", [torch.float16, torch.bfloat16], ids=["fp16", "bf16"])
+@pytest.mark.parametrize("w", RAGGED, ids=lambda w: w.name)
+def test_prefill_ragged(w, kv_dtype):
+    say(f"[prefill ragged] {w.name} B={w.B} T={w.T} H={w.H} {kv_dtype}")
+    inp = workloads.make_inputs(w)
+    out = run_prefill(w, inp, kv_dtype=kv_dtype)
+    assert_close(f64(out), O.prefill(w, inp), f"{w.name} {kv_dtype}",
+                 max_abs=MAX_ABS if kv_dtype == torch.float16 else BF16_MAX_ABS)
+
+
+def test_prefill_bf16_mode_kimi_1k():
+    w = W_["kimi_k2_1k"]
+    say("[prefill] kimi_k2_1k with bf16 intermediates")
+    inp = workloads.make_inputs(w)
+    out = run_prefill(w, inp, kv_dtype=torch.bfloat16)
+    parts = O.prefill_parts(w, inp)
+    ref = np.stack([O.prefill_head(w, parts, 0, h) for h in range(w.H)])[None]
+    assert_close(f64(out), ref, "kimi_k2_1k bf16 mode", max_abs=BF16_MAX_ABS)
+
+
+def test_prefill_empty_is_noop():
+    w = workloads.custom(B=1, T=0, H=2, R=512, Dn=128, Dr=64, Dv=128)
+    q = torch.empty((1, 2, 0, 192), dtype=torch.bfloat16, device="cuda")
+    kn = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
+    kpe = torch.empty((1, 0, 64), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
+    tab = table(w, 1)
+    out = api.mla_prefill_attention(q, kn, kpe, v, tab.cos, tab.sin, tab.scale)
+    assert out.shape == (1, 2, 0, 128)
+
+
+def test_prefill_causality_bitwise():
+    w = workloads.custom(name="causal", B=1, T=600, H=2, R=512, Dn=128, Dr=64, Dv=128, seed=41, rope=workloads.YARN_KIMI)
+    inp = workloads.make_inputs(w)
+    a = run_prefill(w, inp)
+    t0 = 333
+    pert = {k: v.clone() for k, v in inp.items()}
+    pert["q"][:, :, t0 + 1:] = -pert["q"][:, :, t0 + 1:]
+    pert["latent"][:, t0 + 1:] *= 3
+    pert["k_pe"][:, t0 + 1:] += 1
+    b = run_prefill(w, pert)
+    assert torch.equal(a[:, :, :t0 + 1], b[:, :, :t0 + 1])
+    assert not torch.equal(a[:, :, t0 + 1:], b[:, :, t0 + 1:])
+    # run-to-run determinism
+    assert torch.equal(a, run_prefill(w, inp))
+
+
+def test_prefill_properties():
+    w = workloads.custom(name="props", B=1, T=257, H=2, R=512, Dn=128, Dr=64, Dv=128, seed=42)
+    inp = to_gpu(workloads.make_inputs(w))
+    tab = table(w)
+    c = api.mla_latent_rmsnorm(inp["latent"], inp["gain"])
+    kn, v = api.mla_kv_expand(c, inp["W"], w.H, w.Dn, w.Dv)
+    out = api.mla_prefill_attention(inp["q"], kn, inp["k_pe"], v, tab.cos, tab.sin, tab.scale)
+    # row 0 attends to key 0 only: exactly V[0]
+    assert torch.equal(out[:, :, 0], v[:, :, 0])
+    # q = 0: uniform weights -> prefix mean of V
+    z = api.mla_prefill_attention(torch.zeros_like(inp["q"]), kn, inp["k_pe"], v, tab.cos, tab.sin, tab.scale)
+    vf = f64(v)
+    mean = np.cumsum(vf, axis=2) / np.arange(1, w.T + 1)[None, None, :, None]
+    assert_close(f64(z), mean, "q=0 prefix mean", max_abs=2e-2, rel_l2=5e-3)
+
+
+# --------------------------------------------------------------------- decode
+
+def run_decode(w, g, num_splits=0):
+    tab = table(w)
+    seq = torch.full((w.B,), w.cache_len, dtype=torch.int32, device="cuda")
+    qpos = torch.full((w.B,), w.q_pos, dtype=torch.int32, device="cuda")
+    out = pipeline.decode_step(g["q"], g["latent"], g["k_pe"], g["gain"], g["W"], g["k_cache"], g["v_cache"], seq,
+                               qpos, w.q_pos, tab, w.Dn, w.pairing, w.eps, num_splits)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_decode_kimi_full():
+    w = W_["kimi_k2_decode"]
+    say("[decode] kimi_k2_decode B=32 L=1001, all heads")
+    inp = workloads.make_inputs(w)
+    ref = O.decode(w, inp)
+    outs = {}
+    for S in (0, 1, 3, 8):
+        g = to_gpu(inp)
+        outs[S] = run_decode(w, g, S).cpu()
+        del g
+        assert_close(f64(outs[S]), ref, f"decode splits={S or 'auto'}")
+    for S in (1, 3, 8):
+        d = np.abs(f64(outs[S]) - f64(outs[0]))
+        assert np.all(d <= np.abs(f64(outs[0])) * 2.0 ** -7 + 1e-6)
+
+
+@pytest.mark.parametrize("dims", [(32, 16, 32), (128, 64, 128), (192, 64, 256)], ids=["48-32", "192-128", "256-256"])
+def test_decode_ragged_lengths(dims):
+    Dn, Dr, Dv = dims
+    say(f"[decode ragged] dims={dims}")
+    B, H, Tcap = 5, 3, 1100
+    g = torch.Generator().manual_seed(Dn + Dv)
+    cdt = torch.float16 if Dv == 128 else torch.bfloat16  # both cache element types
+    q = torch.randn(B, H, 1, Dn + Dr, generator=g).to(torch.bfloat16)
+    kc = torch.randn(B, H, Tcap, Dn + Dr, generator=g).to(cdt)
+    vc = torch.randn(B, H, Tcap, Dv, generator=g).to(cdt)
+    seq = torch.tensor([1, 17, 600, 1100, 513], dtype=torch.int32)
+    qpos = seq - 1
+    spec = workloads.YARN_KIMI
+    pairing = "interleaved" if Dv == 256 else "half"
+    tab = pipeline.build_table(api.params_from(spec, Dr), Tcap, Dn + Dr)
+    cos, sin = O.rope_table(spec, Dr, Tcap)
+    scale = O.softmax_scale(spec, Dn + Dr)
+    for S in (0, 1, 4):
+        out = api.mla_decode_attention(q.cuda(), kc.cuda(), vc.cuda(), seq.cuda(), qpos.cuda(), tab.cos, tab.sin,
+                                       tab.scale, Dn, pairing, S).cpu()
+        for b in range(B):
+            L = int(seq[b])
+            p = int(qpos[b])
+            for h in range(H):
+                qf = f64(q[b, h, 0])
+                Q = np.concatenate([qf[:Dn], O.rotate(qf[Dn:], cos[p], sin[p], pairing)])[None]
+                ref = O.attention(Q, f64(kc[b, h, :L]), f64(vc[b, h, :L]), scale, np.array([p]), np.arange(L))
+                ma, rl = errors(f64(out[b, h]), ref)
+                assert ma <= MAX_ABS and rl <= REL_L2, (S, b, h, ma, rl)
