@@ -1,0 +1,235 @@
+"""Benchmark of the eager latent-attention forward path on one MI355X.
+
+One step = one pass of the whole hot path:
+  prefill (Kimi-K2 shape, B=2, T=8192, H=64, Dn/Dr/Dv 128/64/128, YaRN):
+    cos/sin table -> latent RMSNorm -> kv_b_proj expansion -> causal attention
+  decode (Kimi-K2 shape, B=32 sequences at position 1000, 1001 cached rows):
+    latent RMSNorm -> kv_b_proj expansion appended into the expanded cache ->
+    split-K decode attention.
+Inputs are drawn on the GPU (same seeded recipe as the parity tests) and are
+resident in HBM before the timed region starts.
+
+Reported (one JSON line):
+  value           prefill-path TFLOP/s (causal attention + kv_b_proj flops over
+                  the measured prefill time of a step)
+  roofline        prefill attention kernel: algorithmic flops per launch over
+                  its mean launch time (HIP events on the launch stream)
+                  against the MI355X dense 16-bit MFMA peak
+  decode          decode attention GB/s (algorithmic bytes) and HBM fraction
+  cpu_baseline    the fp64 CPU oracle on a bounded sample (--cpu-baseline)
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+PREFILL = "kimi_k2_8k"
+DECODE = "kimi_k2_decode"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attn_flops(w) -> float:
+    """Causal attention flops: B*H*T(T+1)/2 key pairs x 2*(Dqk+Dv)."""
+    return w.B * w.H * w.T * (w.T + 1) / 2 * 2 * (w.Dqk + w.Dv)
+
+
+def expand_flops(w) -> float:
+    return 2.0 * w.B * w.T * w.R * w.H * (w.Dn + w.Dv)
+
+
+def decode_bytes(w) -> float:
+    """Algorithmic bytes of decode attention: K and V caches, q and out."""
+    L = w.cache_len
+    return 2.0 * w.B * w.H * (L * (w.Dqk + w.Dv) + w.Dqk + w.Dv)
+
+
+def cpu_baseline(budget_s: float) -> dict:
+    """The fp64 oracle (as is) on a bounded sample of the prefill workload:
+    whole heads of sequence 0 (expansion of that head + causal attention over
+    all 8192 rows), as many as fit in `budget_s` seconds (at least one)."""
+    import dataclasses
+
+    import numpy as np
+
+    import workloads
+    from oracle import mla_oracle as O
+
+    try:
+        import threadpoolctl
+        threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+    w = workloads.WORKLOADS[PREFILL]
+    inp = workloads.make_inputs(dataclasses.replace(w, B=1))
+    wh = dataclasses.replace(w, B=1, H=1)
+    n = w.Dn + w.Dv
+    t0 = time.perf_counter()
+    heads = 0
+    while True:
+        sub = {"q": inp["q"][:, heads:heads + 1], "latent": inp["latent"], "k_pe": inp["k_pe"],
+               "gain": inp["gain"], "W": inp["W"][heads * n:(heads + 1) * n]}
+        parts = O.prefill_parts(wh, sub)
+        O.prefill_head(wh, parts, 0, 0)
+        heads += 1
+        if time.perf_counter() - t0 > budget_s or heads >= w.H:
+            break
+    dt = time.perf_counter() - t0
+    flops = heads * (attn_flops(wh) + expand_flops(wh))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} head(s) of sequence 0 of {PREFILL} (T=8192): fp64 expansion + causal "
+                      f"attention over all rows, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU path is not built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import head_latent_attention_rmsnorm_amd as mla
+    import workloads
+
+    dev = "cuda"
+    wp = workloads.WORKLOADS[PREFILL]
+    wd = workloads.WORKLOADS[DECODE]
+    log(f"[bench] drawing inputs on the GPU: {PREFILL}, {DECODE}")
+    ip = workloads.make_inputs(wp, device=dev)
+    idc = workloads.make_inputs(wd, device=dev)
+    rope_p = mla.api.params_from(wp.rope, wp.Dr)
+    rope_d = mla.api.params_from(wd.rope, wd.Dr)
+    bufs = mla.pipeline.alloc_prefill(wp.B, wp.T, wp.H, wp.R, wp.Dn, wp.Dr, wp.Dv, dev)
+    seq = torch.full((wd.B,), wd.cache_len, dtype=torch.int32, device=dev)
+    qpos = torch.full((wd.B,), wd.q_pos, dtype=torch.int32, device=dev)
+    c_dec = torch.empty((wd.B, 1, wd.R), dtype=torch.float32, device=dev)
+    out_dec = torch.empty((wd.B, wd.H, 1, wd.Dv), dtype=torch.bfloat16, device=dev)
+    splits = args.splits or 0
+    ws_dec = torch.empty((max(1, 64 << 20),), dtype=torch.uint8, device=dev)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    rec = {"prefill": [], "attn": [], "decode": [], "dec_attn": []}
+
+    def step(timed: bool):
+        e = [ev() for _ in range(8)] if timed else None
+        if timed:
+            e[0].record()
+        tab = mla.pipeline.build_table(rope_p, wp.T, wp.Dqk, dev)
+        mla.api.mla_latent_rmsnorm(ip["latent"], ip["gain"], wp.eps, out=bufs.c_norm)
+        mla.api.mla_kv_expand(bufs.c_norm, ip["W"], wp.H, wp.Dn, wp.Dv, k=bufs.k_nope, v=bufs.v)
+        if timed:
+            e[1].record()
+        mla.api.mla_prefill_attention(ip["q"], bufs.k_nope, ip["k_pe"], bufs.v, tab.cos, tab.sin, tab.scale,
+                                      wp.pairing, out=bufs.out, workspace=bufs.workspace)
+        if timed:
+            e[2].record()
+        tdec = mla.pipeline.build_table(rope_d, wd.cache_len, wd.Dqk, dev)
+        mla.api.mla_latent_rmsnorm(idc["latent"], idc["gain"], wd.eps, out=c_dec)
+        mla.api.mla_kv_expand(c_dec, idc["W"], wd.H, wd.Dn, wd.Dv, k=idc["k_cache"], v=idc["v_cache"],
+                              t_off=wd.q_pos, k_pe=idc["k_pe"], cos=tdec.cos, sin=tdec.sin, pos=qpos.view(-1, 1),
+                              pairing=wd.pairing)
+        if timed:
+            e[3].record()
+        mla.api.mla_decode_attention(idc["q"], idc["k_cache"], idc["v_cache"], seq, qpos, tdec.cos, tdec.sin,
+                                     tdec.scale, wd.Dn, wd.pairing, splits, out=out_dec, workspace=ws_dec)
+        if timed:
+            e[4].record()
+        return e
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    evs = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        evs.append(step(True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for e in evs:
+        rec["prefill"].append(e[0].elapsed_time(e[2]))
+        rec["attn"].append(e[1].elapsed_time(e[2]))
+        rec["decode"].append(e[2].elapsed_time(e[4]))
+        rec["dec_attn"].append(e[3].elapsed_time(e[4]))
+    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    ms_step = wall * 1e3 / args.steps
+    t_prefill = mean(rec["prefill"]) * 1e-3
+    t_attn = mean(rec["attn"]) * 1e-3
+    t_dec_attn = mean(rec["dec_attn"]) * 1e-3
+    t_decode = mean(rec["decode"]) * 1e-3
+    fa, fe = attn_flops(wp), expand_flops(wp)
+    value = (fa + fe) / t_prefill / 1e12
+    attn_tflops = fa / t_attn / 1e12
+    dec_gbs = decode_bytes(wd) / t_dec_attn / 1e9
+    log(f"[bench] prefill path {t_prefill * 1e3:.3f} ms ({value:.1f} TFLOP/s), attention {t_attn * 1e3:.3f} ms "
+        f"({attn_tflops:.1f} TFLOP/s, {attn_tflops / MFMA_PEAK_TFLOPS:.1%} of peak); decode step "
+        f"{t_decode * 1e6:.1f} us, decode attention {t_dec_attn * 1e6:.1f} us ({dec_gbs:.0f} GB/s)")
+
+    result = {
+        "metric": "MLA prefill attn TFLOP/s + % bf16 MFMA peak; decode GB/s at 1k ctx",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, fp16 k/v + MFMA, fp32 acc",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{PREFILL} prefill (B=2 T=8192 H=64 R=512 Dn/Dr/Dv=128/64/128 YaRN f=32) + "
+                        f"{DECODE} step (B=32 L=1001 pos 1000)",
+            "prefill_attention_tflops": round(attn_tflops, 2),
+            "prefill_attention_ms": round(t_attn * 1e3, 4),
+            "prefill_path_ms": round(t_prefill * 1e3, 4),
+            "prefill_tokens_per_s": round(wp.B * wp.T / t_prefill, 1),
+            "decode_attention_us": round(t_dec_attn * 1e6, 2),
+            "decode_attention_gbs": round(dec_gbs, 1),
+            "decode_hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "decode_step_us": round(t_decode * 1e6, 2),
+            "decode_tokens_per_s": round(wd.B / t_decode, 1),
+            "decode_splits": splits,
+        },
+        "roofline": {
+            "kernel": "prefill_kernel (causal flash attention, Dqk 192, Dv 128)",
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / MFMA_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (fp64 oracle, ~{args.cpu_budget:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -104,7 +104,7 @@ def custom(name: str = "custom", **kw) -> Workload:
 
 
 def _normal(gen: torch.Generator, shape, std: float = 1.0, mean: float = 0.0) -> torch.Tensor:
-    x = torch.randn(*shape, generator=gen, dtype=torch.float32)
+    x = torch.randn(*shape, generator=gen, dtype=torch.float32, device=gen.device)
     if std != 1.0:
         x = x * std
     if mean != 0.0:
@@ -112,10 +112,14 @@ def _normal(gen: torch.Generator, shape, std: float = 1.0, mean: float = 0.0) ->
     return x.to(torch.bfloat16)
 
 
-def make_inputs(w: Workload, with_cache: bool = True) -> dict:
-    """Draw the workload's bf16 inputs on the CPU.
+def make_inputs(w: Workload, with_cache: bool = True, device: str = "cpu") -> dict:
+    """Draw the workload's bf16 inputs on `device` (default the CPU).
 
-    Returns a dict of CPU bf16 tensors:
+    The recipe is the same on every device; a GPU generator gives a different
+    (equally seeded) random stream from the CPU one, so tests that compare
+    with the oracle draw on the CPU, while benchmarks may draw on the GPU.
+
+    Returns a dict of bf16 tensors on `device`:
       q      [B, H, T, Dn+Dr]   query, rotary part not yet rotated
       latent [B, T, R]          compressed key-value latent (before RMSNorm)
       k_pe   [B, T, Dr]         shared rotary key, not yet rotated
@@ -127,7 +131,7 @@ def make_inputs(w: Workload, with_cache: bool = True) -> dict:
     where the new token's row (slot q_pos) of both caches is the one the
     decode step overwrites.
     """
-    gen = torch.Generator(device="cpu")
+    gen = torch.Generator(device=device)
     gen.manual_seed(w.seed)
     out = {
         "q": _normal(gen, (w.B, w.H, w.T, w.Dqk)),
