@@ -79,6 +79,8 @@ struct BF16 {
   // low / high element of a packed pair
   __device__ static __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
   __device__ static __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  // acc + both elements of a packed pair
+  __device__ static __forceinline__ float sum2(uint32_t w, float acc) { return acc + lo(w) + hi(w); }
   __device__ static __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                    0, 0, 0);
@@ -92,10 +94,25 @@ struct F16 {
   __device__ static __forceinline__ uint32_t pack2(float a, float b) { return pack2h(a, b); }
   __device__ static __forceinline__ float lo(uint32_t w) { return h2f((uint16_t)(w & 0xffffu)); }
   __device__ static __forceinline__ float hi(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
+  __device__ static __forceinline__ float sum2(uint32_t w, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
+  }
   __device__ static __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
                                                   0, 0);
   }
 };
+
+// Raw buffer resource over [base, base + bytes): loads at byte offsets past
+// the end return zeros (the hardware range check), which replaces per-lane
+// bounds branches for ragged tiles. Offsets are passed in the vector offset
+// (the one the range check covers); the tensor slice must be < 4 GiB.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
 
 }  // namespace mla
