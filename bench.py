@@ -56,6 +56,27 @@ def decode_bytes(w) -> float:
     return 2.0 * w.B * w.H * (L * (w.Dqk + w.Dv) + w.Dqk + w.Dv)
 
 
+def measured_traffic(kernel_source: str, key=None):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain device copy),
+    or None when the kernel's source has changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if key:
+        rec = rec.get(key, {})
+    src = os.path.join(ROOT, kernel_source)
+    if rec.get("source") != kernel_source or not os.path.exists(src):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("source_sha256"):
+        return None
+    return int(round(rec["fetch_bytes"] + rec["write_bytes"]))
+
+
 def cpu_baseline(budget_s: float) -> dict:
     """The fp64 oracle (as is) on a bounded sample of the prefill workload:
     whole heads of sequence 0 (expansion of that head + causal attention over
@@ -101,6 +122,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB first (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU path is not built.",
@@ -127,6 +150,15 @@ def main():
     out_dec = torch.empty((wd.B, wd.H, 1, wd.Dv), dtype=torch.bfloat16, device=dev)
     splits = args.splits or 0
     ws_dec = torch.empty((max(1, 64 << 20),), dtype=torch.uint8, device=dev)
+
+    if args.calib_copy_mib:
+        src = torch.empty((args.calib_copy_mib << 20,), dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
+        del src, dst
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     rec = {"prefill": [], "attn": [], "decode": [], "dec_attn": []}
@@ -214,6 +246,9 @@ def main():
             "decode_step_us": round(t_decode * 1e6, 2),
             "decode_tokens_per_s": round(wd.B / t_decode, 1),
             "decode_splits": splits,
+            "decode_traffic_bytes": measured_traffic("head_latent_attention_rmsnorm_amd/csrc/decode_attn.hip",
+                                                     "decode"),
+            "decode_algorithmic_bytes": int(decode_bytes(wd)),
         },
         "roofline": {
             "kernel": "prefill_kernel (causal flash attention, Dqk 192, Dv 128)",
@@ -222,7 +257,7 @@ def main():
             "peak": MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / MFMA_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("head_latent_attention_rmsnorm_amd/csrc/prefill_attn.hip"),
         },
     }
     if not args.no_cpu_baseline:
