@@ -169,11 +169,11 @@ def main():
             e[0].record()
         tab = mla.pipeline.build_table(rope_p, wp.T, wp.Dqk, dev)
         mla.api.mla_latent_rmsnorm(ip["latent"], ip["gain"], wp.eps, out=bufs.c_norm)
-        mla.api.mla_kv_expand(bufs.c_norm, ip["W"], wp.H, wp.Dn, wp.Dv, k=bufs.k_nope, v=bufs.v)
+        mla.api.mla_kv_expand(bufs.c_norm, ip["W"], wp.H, wp.Dn, wp.Dv, k=bufs.k_nope, v=bufs.v, v_layout="cols")
         if timed:
             e[1].record()
         mla.api.mla_prefill_attention(ip["q"], bufs.k_nope, ip["k_pe"], bufs.v, tab.cos, tab.sin, tab.scale,
-                                      wp.pairing, out=bufs.out, workspace=bufs.workspace)
+                                      wp.pairing, out=bufs.out, workspace=bufs.workspace, v_layout="cols")
         if timed:
             e[2].record()
         tdec = mla.pipeline.build_table(rope_d, wd.cache_len, wd.Dqk, dev)

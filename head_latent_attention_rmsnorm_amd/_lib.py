@@ -26,6 +26,7 @@ STATUS = {
 ROPE_DEFAULT, ROPE_YARN = 0, 1
 PAIR_HALF, PAIR_INTERLEAVED = 0, 1
 DTYPE_BF16, DTYPE_FP16 = 0, 1
+V_ROWS, V_COLS = 0, 1
 
 # every symbol the header declares
 EXPORTS = [
@@ -76,10 +77,10 @@ def load() -> ctypes.CDLL:
     lib.mla_rope_table_build.argtypes = [ctypes.POINTER(RopeParams), I32, P, P, ctypes.POINTER(ctypes.c_double), P]
     lib.mla_softmax_scale.argtypes = [ctypes.POINTER(RopeParams), I32, ctypes.POINTER(ctypes.c_double)]
     lib.mla_latent_rmsnorm.argtypes = [P, P, F32, P, I32, I32, P]
-    lib.mla_kv_expand.argtypes = [P, P, I32, I32, I32, I32, I32, I32, P, I32, P, I32, I32, I32, P, P, P, I32, P,
-                                  I32, I32, P]
-    lib.mla_prefill_attention.argtypes = [P, P, P, P, I32, P, P, I32, P, I32, I32, I32, I32, I32, I32, F32, I32, P,
-                                          P, P, SZ, P]
+    lib.mla_kv_expand.argtypes = [P, P, I32, I32, I32, I32, I32, I32, P, I32, P, I32, I32, I32, I32, I32, P, P, P,
+                                  I32, P, I32, I32, P]
+    lib.mla_prefill_attention.argtypes = [P, P, P, P, I32, I32, I32, P, P, I32, P, I32, I32, I32, I32, I32, I32, F32,
+                                          I32, P, P, P, SZ, P]
     lib.mla_decode_attention.argtypes = [P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F32, I32, I32,
                                          P, SZ, P, P]
     for name in EXPORTS[:-1]:

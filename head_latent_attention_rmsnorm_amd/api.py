@@ -116,33 +116,52 @@ def mla_latent_rmsnorm(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
     return y
 
 
+def _layout_code(v_layout: str) -> int:
+    if v_layout == "rows":
+        return _lib.V_ROWS
+    if v_layout == "cols":
+        return _lib.V_COLS
+    raise ValueError(f"v_layout must be 'rows' or 'cols', not {v_layout!r}")
+
+
+def round8(n: int) -> int:
+    return (n + 7) // 8 * 8
+
+
 def mla_kv_expand(c_norm: torch.Tensor, W: torch.Tensor, H: int, Dn: int, Dv: int,
                   k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None, t_off: int = 0,
                   k_pe: Optional[torch.Tensor] = None, cos: Optional[torch.Tensor] = None,
                   sin: Optional[torch.Tensor] = None, pos: Optional[torch.Tensor] = None,
-                  pairing="half", kv_dtype=torch.float16) -> Tuple[torch.Tensor, torch.Tensor]:
+                  pairing="half", kv_dtype=torch.float16, v_layout: str = "rows") -> Tuple[torch.Tensor, torch.Tensor]:
     """kv_b_proj of c_norm (fp32 [B, T, R]) by W (bf16 [H*(Dn+Dv), R]).
 
-    Without k/v: returns new k_nope [B, H, T, Dn] and v [B, H, T, Dv].
-    New tensors take `kv_dtype` (bf16 or fp16); given k and v must share
-    one of those element types.
-    With k [B, H, Tcap, k_ld] and v [B, H, Tcap, Dv]: writes rows
-    t_off .. t_off+T-1; with k_pe [B, T, Dr] also writes the rotated shared
-    key into k[..., Dn:Dn+Dr] of every head (append mode)."""
+    Without k/v: returns new k_nope [B, H, T, Dn] and v, [B, H, T, Dv] for
+    v_layout "rows" or V^T [B, H, Dv, round8(T)] for "cols" (padding columns
+    zeroed). New tensors take `kv_dtype` (bf16 or fp16); given k and v must
+    share one of those element types.
+    With k [B, H, Tcap, k_ld] and v [B, H, Tcap, Dv] (or V^T [B, H, Dv, v_ld]):
+    writes rows (columns) t_off .. t_off+T-1; with k_pe [B, T, Dr] also writes
+    the rotated shared key into k[..., Dn:Dn+Dr] of every head (append mode)."""
     _need(c_norm, "c_norm", torch.float32)
     _need(W, "W")
+    lcode = _layout_code(v_layout)
     B, T, R = c_norm.shape
     if k is None:
         k = torch.empty((B, H, T, Dn), dtype=kv_dtype, device=c_norm.device)
+    Tcap = k.shape[2]
     if v is None:
-        v = torch.empty((B, H, k.shape[2], Dv), dtype=k.dtype, device=c_norm.device)
+        shape = (B, H, Tcap, Dv) if lcode == _lib.V_ROWS else (B, H, Dv, round8(Tcap))
+        v = torch.empty(shape, dtype=k.dtype, device=c_norm.device)
     code = _kv_code(k, "k")
     _need(k, "k", k.dtype)
     _need(v, "v", k.dtype)
     _shape(W, "W", (H * (Dn + Dv), R))
     if k.dim() != 4 or tuple(k.shape[:2]) != (B, H):
         raise ValueError(f"k should be [B={B}, H={H}, Tcap, k_ld], but is {tuple(k.shape)}")
-    _shape(v, "v", (B, H, k.shape[2], Dv))
+    if lcode == _lib.V_ROWS:
+        _shape(v, "v", (B, H, Tcap, Dv))
+    elif v.dim() != 4 or tuple(v.shape[:3]) != (B, H, Dv):
+        raise ValueError(f"v (V^T) should be [B={B}, H={H}, Dv={Dv}, v_ld], but is {tuple(v.shape)}")
     Dr = 0
     table_len = 0
     if k_pe is not None:
@@ -159,23 +178,26 @@ def mla_kv_expand(c_norm: torch.Tensor, W: torch.Tensor, H: int, Dn: int, Dv: in
         _need(pos, "pos", torch.int32)
         _shape(pos, "pos", (B, T))
     check("mla_kv_expand",
-          _lib.load().mla_kv_expand(_ptr(c_norm), _ptr(W), B, T, R, H, Dn, Dv, _ptr(k), k.shape[-1], _ptr(v),
-                                    k.shape[2], int(t_off), code, _ptr(k_pe), _ptr(cos), _ptr(sin), table_len,
-                                    _ptr(pos), Dr, pairing_code(pairing), _stream(c_norm)))
+          _lib.load().mla_kv_expand(_ptr(c_norm), _ptr(W), B, T, R, H, Dn, Dv, _ptr(k), k.shape[-1], _ptr(v), lcode,
+                                    v.shape[-1], Tcap, int(t_off), code, _ptr(k_pe), _ptr(cos), _ptr(sin),
+                                    table_len, _ptr(pos), Dr, pairing_code(pairing), _stream(c_norm)))
     return k, v
 
 
 def mla_prefill_attention(q: torch.Tensor, k_nope: torch.Tensor, k_pe: torch.Tensor, v: torch.Tensor,
                           cos: torch.Tensor, sin: torch.Tensor, scale: float, pairing="half",
                           pos: Optional[torch.Tensor] = None, return_lse: bool = False,
-                          out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+                          out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                          v_layout: str = "rows"):
     """Causal attention out [B, H, T, Dv] bf16 (and lse [B, H, T] fp32).
 
-    q [B, H, T, Dn+Dr] bf16, k_nope [B, H, T, Dn] and v [B, H, T, Dv] (both
-    bf16 or both fp16), k_pe [B, T, Dr] bf16 (not rotated), cos/sin
-    [table_len, Dr/2] fp32."""
+    q [B, H, T, Dn+Dr] bf16, k_nope [B, H, T, Dn] and v (both bf16 or both
+    fp16; v [B, H, T, Dv] for v_layout "rows", V^T [B, H, Dv, v_ld] for
+    "cols"), k_pe [B, T, Dr] bf16 (not rotated), cos/sin [table_len, Dr/2]
+    fp32."""
     for t, n in ((q, "q"), (k_pe, "k_pe")):
         _need(t, n)
+    lcode = _layout_code(v_layout)
     code = _kv_code(k_nope, "k_nope")
     _need(k_nope, "k_nope", k_nope.dtype)
     _need(v, "v", k_nope.dtype)
@@ -184,10 +206,15 @@ def mla_prefill_attention(q: torch.Tensor, k_nope: torch.Tensor, k_pe: torch.Ten
     B, H, T, Dqk = q.shape
     Dn = k_nope.shape[-1]
     Dr = k_pe.shape[-1]
-    Dv = v.shape[-1]
     _shape(k_nope, "k_nope", (B, H, T, Dqk - Dr))
     _shape(k_pe, "k_pe", (B, T, Dr))
-    _shape(v, "v", (B, H, T, Dv))
+    if lcode == _lib.V_ROWS:
+        Dv, v_ld = v.shape[-1], 0
+        _shape(v, "v", (B, H, T, Dv))
+    else:
+        if v.dim() != 4 or tuple(v.shape[:2]) != (B, H):
+            raise ValueError(f"v (V^T) should be [B={B}, H={H}, Dv, v_ld], but is {tuple(v.shape)}")
+        Dv, v_ld = v.shape[2], v.shape[3]
     _shape(sin, "sin", cos.shape)
     if cos.dim() != 2 or cos.shape[1] != Dr // 2:
         raise ValueError(f"cos should be [table_len, {Dr // 2}], but is {tuple(cos.shape)}")
@@ -201,8 +228,8 @@ def mla_prefill_attention(q: torch.Tensor, k_nope: torch.Tensor, k_pe: torch.Ten
         _need(pos, "pos", torch.int32)
         _shape(pos, "pos", (B, T))
     need = ctypes.c_size_t(0)
-    args_head = (_ptr(q), _ptr(k_nope), _ptr(k_pe), _ptr(v), code, _ptr(cos), _ptr(sin), cos.shape[0], _ptr(pos), B, H,
-                 T, Dn, Dr, Dv, float(scale), pairing_code(pairing), _ptr(out), _ptr(lse))
+    args_head = (_ptr(q), _ptr(k_nope), _ptr(k_pe), _ptr(v), lcode, v_ld, code, _ptr(cos), _ptr(sin), cos.shape[0],
+                 _ptr(pos), B, H, T, Dn, Dr, Dv, float(scale), pairing_code(pairing), _ptr(out), _ptr(lse))
     check("mla_prefill_attention", lib.mla_prefill_attention(*args_head, None, ctypes.byref(need), _stream(q)))
     if workspace is None or workspace.numel() < need.value:
         workspace = torch.empty((max(need.value, 1),), dtype=torch.uint8, device=q.device)

@@ -128,10 +128,12 @@ mla_status mla_latent_rmsnorm(const mla_bf16* x, const mla_bf16* w, float eps, f
 }
 
 mla_status mla_kv_expand(const float* c_norm, const mla_bf16* W, int32_t B, int32_t T, int32_t R, int32_t H,
-                         int32_t Dn, int32_t Dv, uint16_t* k, int32_t k_ld, uint16_t* v, int32_t Tcap, int32_t t_off,
-                         int32_t kv_dtype, const mla_bf16* k_pe, const float* cos, const float* sin,
-                         int32_t table_len, const int32_t* pos, int32_t Dr, int32_t pairing, hipStream_t stream) {
+                         int32_t Dn, int32_t Dv, uint16_t* k, int32_t k_ld, uint16_t* v, int32_t v_layout,
+                         int32_t v_ld, int32_t Tcap, int32_t t_off, int32_t kv_dtype, const mla_bf16* k_pe,
+                         const float* cos, const float* sin, int32_t table_len, const int32_t* pos, int32_t Dr,
+                         int32_t pairing, hipStream_t stream) {
   if (!dtype_ok(kv_dtype)) return MLA_ERR_UNSUPPORTED;
+  if (v_layout != MLA_V_ROWS && v_layout != MLA_V_COLS) return MLA_ERR_SHAPE;
   if (B < 0 || T < 0) return MLA_ERR_SHAPE;
   if ((int64_t)B * T == 0) return MLA_OK;
   if (!c_norm || !W || !k || !v) return MLA_ERR_NULL;
@@ -141,6 +143,8 @@ mla_status mla_kv_expand(const float* c_norm, const mla_bf16* W, int32_t B, int3
   if (k_ld < Dn || (k_ld % 8)) return MLA_ERR_SHAPE;
   if ((int64_t)B * T > ((int64_t)1 << 30) || (int64_t)H * (Dn + Dv) > ((int64_t)1 << 30)) return MLA_ERR_SHAPE;
   if ((int64_t)B * H * Tcap * (int64_t)(k_ld > Dv ? k_ld : Dv) > kMaxElems) return MLA_ERR_SHAPE;
+  if (v_layout == MLA_V_COLS && (v_ld < Tcap || (v_ld % 8) || (int64_t)B * H * Dv * v_ld > kMaxElems))
+    return MLA_ERR_SHAPE;
   if (!aligned16(c_norm) || !aligned16(W) || !aligned16(k) || !aligned16(v)) return MLA_ERR_SHAPE;
   const bool append = k_pe != nullptr;
   if (append) {
@@ -149,7 +153,8 @@ mla_status mla_kv_expand(const float* c_norm, const mla_bf16* W, int32_t B, int3
     if (Dr < 2 || (Dr & 1) || Dr > 256 || k_ld < Dn + Dr || table_len < 1) return MLA_ERR_SHAPE;
     if (!pos && t_off + T > table_len) return MLA_ERR_SHAPE;
   }
-  mla::ExpandArgs a{c_norm, W, k, v, B, T, R, H, Dn, Dv, k_ld, Tcap, t_off, kv_dtype};
+  mla::ExpandArgs a{c_norm, W, k, v, B, T, R, H, Dn, Dv, k_ld, Tcap, t_off, kv_dtype, v_layout == MLA_V_COLS,
+                    v_layout == MLA_V_COLS ? v_ld : 0};
   clear_stale_error();
   hipError_t e = mla::launch_kv_expand(a, stream);
   if (e != hipSuccess) return MLA_ERR_HIP;
@@ -160,23 +165,33 @@ mla_status mla_kv_expand(const float* c_norm, const mla_bf16* W, int32_t B, int3
   return hip_status(e);
 }
 
-static size_t prefill_ws(int32_t B, int32_t T, int32_t Dr) {
-  return (((size_t)B * T * Dr * sizeof(uint16_t)) + 255) / 256 * 256;
+static size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Workspace of the prefill: the rotated shared rotary key [B, T, Dr], then
+// (row-major values only) their transposed copy [B, H, Dv, round8(T)].
+static size_t prefill_ws(int32_t B, int32_t H, int32_t T, int32_t Dr, int32_t Dv, int32_t v_layout) {
+  size_t n = round256((size_t)B * T * Dr * sizeof(uint16_t));
+  if (v_layout == MLA_V_ROWS) n += round256((size_t)B * H * Dv * (size_t)((T + 7) / 8 * 8) * sizeof(uint16_t));
+  return n;
 }
 
 mla_status mla_prefill_attention(const mla_bf16* q, const uint16_t* k_nope, const mla_bf16* k_pe, const uint16_t* v,
-                                 int32_t kv_dtype, const float* cos, const float* sin, int32_t table_len,
-                                 const int32_t* pos,
-                                 int32_t B, int32_t H, int32_t T, int32_t Dn, int32_t Dr, int32_t Dv, float scale,
-                                 int32_t pairing, mla_bf16* out, float* lse, void* workspace, size_t* ws_bytes,
-                                 hipStream_t stream) {
+                                 int32_t v_layout, int32_t v_ld, int32_t kv_dtype, const float* cos,
+                                 const float* sin, int32_t table_len, const int32_t* pos, int32_t B, int32_t H,
+                                 int32_t T, int32_t Dn, int32_t Dr, int32_t Dv, float scale, int32_t pairing,
+                                 mla_bf16* out, float* lse, void* workspace, size_t* ws_bytes, hipStream_t stream) {
   if (B < 0 || H < 1 || T < 0 || Dn < 1 || Dr < 2 || (Dr & 1) || Dv < 1) return MLA_ERR_SHAPE;
+  if (v_layout != MLA_V_ROWS && v_layout != MLA_V_COLS) return MLA_ERR_SHAPE;
   if (!mla::prefill_supported(Dn + Dr, Dr, Dv) || !dtype_ok(kv_dtype)) return MLA_ERR_UNSUPPORTED;
   if (!pairing_ok(pairing)) return MLA_ERR_ROPE_TYPE;
   if ((int64_t)B * H * T * (Dn + Dr) > kMaxElems || (int64_t)B * H > ((int64_t)1 << 24) ||
       (int64_t)T > ((int64_t)1 << 26))
     return MLA_ERR_SHAPE;
-  const size_t need = prefill_ws(B, T, Dr);
+  const int32_t Tv = v_layout == MLA_V_COLS ? v_ld : (T + 7) / 8 * 8;
+  if (v_layout == MLA_V_COLS && (v_ld < T || (v_ld % 8))) return MLA_ERR_SHAPE;
+  // one (b, h) slice of every operand is addressed with 32-bit byte offsets
+  if ((int64_t)T * (Dn > Dv ? Dn : Dv) * 2 > 0x7fffffff || (int64_t)Dv * Tv * 2 > 0x7fffffff) return MLA_ERR_SHAPE;
+  const size_t need = prefill_ws(B, H, T, Dr, Dv, v_layout);
   if (!workspace && ws_bytes) {
     *ws_bytes = need;
     return MLA_OK;
@@ -194,8 +209,16 @@ mla_status mla_prefill_attention(const mla_bf16* q, const uint16_t* k_nope, cons
   mla::RotKeyArgs r{k_pe, cos, sin, table_len, pos, k_rot, B, T, 1, Dr, T, 0, Dr, 0, pairing, kv_dtype};
   hipError_t e = mla::launch_rotate_key(r, stream);
   if (e != hipSuccess) return MLA_ERR_HIP;
-  mla::PrefillArgs a{q, k_nope, k_rot, v, cos, sin, table_len, pos, out, lse, B, H, T, Dn, Dr, Dv, pairing, scale,
-                     kv_dtype};
+  const uint16_t* vt = v;
+  if (v_layout == MLA_V_ROWS) {
+    uint16_t* vt_ws = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) +
+                                                  round256((size_t)B * T * Dr * sizeof(uint16_t)));
+    e = mla::launch_transpose_v(v, vt_ws, B * H, T, Dv, Tv, stream);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    vt = vt_ws;
+  }
+  mla::PrefillArgs a{q, k_nope, k_rot, vt, cos, sin, table_len, pos, out, lse, B, H, T, Dn, Dr, Dv, pairing, scale,
+                     kv_dtype, Tv};
   return hip_status(mla::launch_prefill(a, stream));
 }
 

@@ -15,6 +15,10 @@
 // 4-column group never straddles a head or the k/v boundary because Dn and Dv
 // are multiples of 8).
 //
+// With v_cols set, values are written transposed (V^T [B, H, Dv, v_ld], the
+// layout the prefill attention reads): one 2-byte store per value, 32
+// consecutive tokens per store instruction.
+//
 // Workgroup tile 128 n x 128 tokens, 4 waves in 2x2, each 64 x 64 (2x2 MFMA
 // tiles); K staged 32 at a time, double-buffered in LDS with a 16-byte row
 // pad; global loads for stage s+1 are in flight while stage s is multiplied.
@@ -152,6 +156,19 @@ __global__ void __launch_bounds__(256, 2) kv_expand_kernel(ExpandArgs a, int M, 
         const int h = n / DnDv;
         const int c = n - h * DnDv;
         const size_t rowi = ((size_t)b * a.H + h) * a.Tcap + a.t_off + t;
+        if (c >= a.Dn && a.v_cols) {
+          // V^T: the four value columns are four rows of [Dv, v_ld]; the lane
+          // writing the cache's last column also zeroes the row padding
+          const int col = a.t_off + t;
+          uint16_t* dst = a.v + (((size_t)b * a.H + h) * a.Dv + (c - a.Dn)) * a.v_ld + col;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dst[(size_t)e * a.v_ld] = ET::enc(acc[i][j][g * 4 + e]);
+            if (col == a.Tcap - 1)
+              for (int z = col + 1; z < a.v_ld; ++z) dst[(size_t)e * a.v_ld + (z - col)] = 0;
+          }
+          continue;
+        }
         uint16_t* dst = (c < a.Dn) ? a.k + rowi * a.k_ld + c : a.v + rowi * a.Dv + (c - a.Dn);
         u32x2 o;
         o[0] = ET::pack2(acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1]);

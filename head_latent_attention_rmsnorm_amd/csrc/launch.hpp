@@ -31,9 +31,11 @@ struct ExpandArgs {
   const float* c;     // [B*T, R] normalised latent, fp32
   const uint16_t* W;  // [N, R], N = H*(Dn+Dv)
   uint16_t* k;        // [B, H, Tcap, k_ld]
-  uint16_t* v;        // [B, H, Tcap, Dv]
+  uint16_t* v;        // [B, H, Tcap, Dv] (v_cols == 0) or [B, H, Dv, v_ld] (v_cols == 1)
   int B, T, R, H, Dn, Dv, k_ld, Tcap, t_off;
   int kv_dtype;       // element type of k and v: 0 bf16, 1 fp16
+  int v_cols;         // values stored transposed (V^T)
+  int v_ld;           // row stride of V^T (>= Tcap); columns Tcap..v_ld-1 are zeroed
 };
 hipError_t launch_kv_expand(const ExpandArgs& a, hipStream_t stream);
 
@@ -57,7 +59,7 @@ struct PrefillArgs {
   const uint16_t* q;       // [B, H, T, Dqk]
   const uint16_t* k_nope;  // [B, H, T, Dn]  (kv_dtype)
   const uint16_t* k_rot;   // [B, T, Dr] rotated (workspace, kv_dtype)
-  const uint16_t* v;       // [B, H, T, Dv]  (kv_dtype)
+  const uint16_t* v;       // V^T [B, H, Dv, v_ld] (kv_dtype), columns T..v_ld-1 finite
   const float* cos;
   const float* sin;
   int table_len;
@@ -67,9 +69,12 @@ struct PrefillArgs {
   int B, H, T, Dn, Dr, Dv, pairing;
   float scale;
   int kv_dtype;  // 0 bf16, 1 fp16
+  int v_ld;      // row stride of V^T, a multiple of 8, >= T
 };
 bool prefill_supported(int Dqk, int Dr, int Dv);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// row-major values [BH, T, Dv] -> V^T [BH, Dv, v_ld], columns T..v_ld-1 zero
+hipError_t launch_transpose_v(const uint16_t* v, uint16_t* vt, int BH, int T, int Dv, int v_ld, hipStream_t stream);
 
 struct DecodeArgs {
   const uint16_t* q;        // [B, H, 1, Dqk]

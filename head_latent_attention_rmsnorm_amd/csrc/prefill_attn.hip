@@ -8,37 +8,50 @@
 //
 // Design (gfx950, 64-wide wavefronts, 16-bit MFMA 32x32x16 with fp32
 // accumulation; operands in the key/value element type, bf16 or fp16):
-//  - workgroup = (sequence b, head h, NW*32 query rows), NW waves of 32 rows,
-//    two waves per SIMD;
+//  - workgroup = (sequence b, head h, NW*32 query rows), NW waves of 32 rows;
+//    with 8 waves the row blocks are dealt so that the two waves sharing a
+//    SIMD (w and w+4) get blocks s and 7-s, which evens out the triangular
+//    work of the diagonal tiles;
 //  - each wave keeps its 32 rotated query rows in registers as the B operand
 //    of S^T = K Q^T, so the score accumulator has one query per lane and the
 //    softmax statistics are per-lane values (lane l and l^32 share a query);
-//  - K tiles (k_nope | pre-rotated shared k_pe) and V^T tiles are double-
-//    buffered in LDS with one barrier per tile; they are fetched with raw
-//    buffer loads whose range check returns zeros past the end of the
-//    sequence, so no load is predicated;
-//  - inside each 32-key sub-tile the K rows are fed to the MFMA in a permuted
-//    order, chosen so that the 8 scores a lane holds for one 16-key step of
-//    P V are 8 consecutive keys: P goes from the S accumulator to a 16-bit B
-//    operand of O^T = V^T P^T with no data movement, and V^T is read with
-//    16-byte LDS loads;
+//  - values arrive transposed (V^T, keys contiguous per value column), so
+//    both products read their A operands as 8 consecutive 16-bit elements;
+//  - K and V^T tiles move global -> LDS with 16-byte buffer loads that write
+//    LDS directly (no registers, no LDS store instructions). The LDS image is
+//    fragment-major: one 1 KB block per (32-key sub-tile, 16-deep k-step) or
+//    (32-value tile, 16-key step) holds the 64 lanes' MFMA operands in lane
+//    order, so every operand read is one conflict-free 16-byte LDS read. The
+//    gather into that order happens in the loads' per-lane addresses, which
+//    stay fixed over the key loop (the tile offset moves the buffer
+//    descriptor's base); the descriptor's range check returns zeros past the
+//    end of the sequence. Tiles are double-buffered, one barrier per tile;
+//  - the K rows of a 32-key sub-tile are gathered in a permuted order, chosen
+//    so that the 8 scores a lane holds for one 16-key step of P V are 8
+//    consecutive keys: P goes from the S accumulator to a 16-bit B operand of
+//    O^T = V^T P^T with no data movement;
 //  - all K fragments of a sub-tile are read from LDS before its MFMAs start
 //    (a scheduling fence keeps them in flight together);
 //  - MFMA and VALU work hardly overlap on this chip, so the softmax is cut to
 //    the bone: in fp16 mode the query is pre-scaled by scale*log2(e) and the
 //    first MFMA of every score chain accumulates onto -m (the running
-//    reference maximum), so the scores leave the MFMA already as exp2
-//    arguments; the reference is raised only when a score exceeds it by more
-//    than 2^8 (exact: O and the row sum share the reference);
-//  - row sums come from v_dot2 over the packed 16-bit P (the values the PV
-//    MFMA consumes), and the transposed V store builds each word with one
-//    byte permute;
+//    reference maximum), so the scores leave the MFMA as exp2 arguments. The
+//    reference only moves when this tile's P would leave a safe range: the
+//    per-lane sum of the tile's P (taken anyway, with v_dot2 on the packed
+//    16-bit P that the PV product consumes) bounds every P, and only when it
+//    exceeds 2^14 (or on the first tile) is the exact tile maximum taken and
+//    the reference raised to it (exact: O and the row sum share the
+//    reference);
 //  - only the tiles crossing a wave's diagonal are masked; tiles above it are
-//    never loaded;
+//    neither loaded nor multiplied;
 //  - workgroup ids are dealt to the 8 XCDs round-robin; the id -> (b, h,
 //    q-tile) map makes XCD x run (b, h) pairs x, x+8, ... one at a time,
 //    heaviest query tile first, so a pair's keys and values stay in that
 //    XCD's L2.
+//
+// A second kernel transposes row-major values [B, H, T, Dv] into the V^T
+// layout [B, H, Dv, Tv] (Tv = T rounded up to 8, zero-filled) when the caller
+// does not already hold them transposed.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -48,34 +61,34 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units
+constexpr float kSumLimit = 16384.0f;  // per-lane tile sum of P that triggers the exact maximum
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, 0, 0, 0);
+}
 }  // namespace
 
 template <class ET, int DQK, int DR, int DV, int BN, int NW, int MINW>
 __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, int nqt) {
-  constexpr int NT = 64 * NW;           // threads per workgroup
   constexpr int DN = DQK - DR;
   constexpr int QC = DQK / 16;          // 16-deep MFMA steps over the head dim
-  constexpr int LDQ = DQK + 8;          // K tile row stride (16-bit elements)
-  constexpr int LDV = BN + 8;           // V^T tile row stride
-  constexpr int BMW = NW * 32;          // query rows per workgroup
-  constexpr int NCH_N = BN * (DN / 8);  // 16-byte non-rotary chunks per K tile
-  constexpr int NCH_R = BN * (DR / 8);  // 16-byte rotary chunks per K tile
-  constexpr int PER_N = (NCH_N + NT - 1) / NT;
-  constexpr int PER_R = (NCH_R + NT - 1) / NT;
-  constexpr int VUNITS = (BN / 4) * (DV / 8);  // (4 keys x 8 values) units
-  constexpr int VPER = (VUNITS + NT - 1) / NT;
   constexpr int NSUB = BN / 32;         // 32-key sub-tiles
   constexpr int NPV = BN / 16;          // 16-key PV steps
   constexpr int NO = DV / 32;           // 32-wide value tiles
+  constexpr int KBLK = NSUB * QC;       // K operand blocks (1 KB) per tile
+  constexpr int NBLK = KBLK + NO * NPV; // K + V^T operand blocks per tile
+  constexpr int LPW = (NBLK + NW - 1) / NW;  // LDS-direct loads per wave per tile
+  constexpr int BMW = NW * 32;          // query rows per workgroup
   constexpr bool FOLD = ET::code == F16::code;  // scores leave the MFMA as exp2 arguments
-  static_assert(DN % 8 == 0 && DR % 16 == 0 && DV % 32 == 0 && BN % 32 == 0, "tile shape");
+  static_assert(DN % 16 == 0 && DR % 16 == 0 && DV % 32 == 0 && BN % 32 == 0, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * LDQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][DV * LDV];
+  __shared__ __attribute__((aligned(16))) u32x4 smem[2][NBLK * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int HB = a.H * a.B;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int hb = xcd + 8 * (slot / nqt);
@@ -85,16 +98,13 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
   const int b = hb / a.H;
   const int T = a.T;
   const size_t bh = (size_t)b * a.H + h;
-
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_nope + bh * T * DN, (uint32_t)T * DN * 2);
-  const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.k_rot + (size_t)b * T * DR, (uint32_t)T * DR * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + bh * T * DV, (uint32_t)T * DV * 2);
   const uint16_t* qg = a.q + bh * T * DQK;
 
   const int l32 = lane & 31;
   const int g = lane >> 5;
-  const int qlo = qt * BMW + wave * 32;  // first query row of this wave
-  const int tq = qlo + l32;              // this lane's query row
+  const int rb = (NW == 8 && wave >= 4) ? 11 - wave : wave;  // row block of this wave
+  const int qlo = qt * BMW + rb * 32;  // first query row of this wave
+  const int tq = qlo + l32;            // this lane's query row
   const float sl2 = a.scale * kLog2e;
   const float qmul = FOLD ? sl2 : 1.0f;  // query pre-scale
 
@@ -157,69 +167,54 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
     }
   }
 
+
   const int kend = min(T, (qt + 1) * BMW);  // keys [0, kend) are visible to some row
   const int nkt = (kend + BN - 1) / BN;
 
-  // ---- tile staging: global -> registers -> LDS
-  u32x4 kn_reg[PER_N], kr_reg[PER_R];
-  u32x4 v_reg[VPER][4];
-  auto gload = [&](int kt) {
+  // K row gathered by this lane for the S^T MFMA: the permutation that makes
+  // the lane's accumulator registers 8*(r>>3) .. hold consecutive keys
+  const int krow = 16 * ((l32 >> 3) >> 1) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
+
+  // per-lane byte offsets of this wave's operand blocks, relative to the
+  // tile's first key (fixed over the key loop)
+  uint32_t voff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int bi = wave + NW * i;
+    uint32_t o = 0;
+    if (bi < KBLK) {
+      const int j = bi / QC, c = bi % QC;
+      const int row = 32 * j + krow;
+      o = (16 * c < DN) ? (uint32_t)(row * DN + 16 * c + 8 * g) * 2u
+                        : (uint32_t)(row * DR + (16 * c - DN) + 8 * g) * 2u;
+    } else if (bi < NBLK) {
+      const int vb = bi - KBLK, d = vb / NPV, m = vb % NPV;
+      o = (uint32_t)((32 * d + l32) * a.v_ld + 16 * m + 8 * g) * 2u;
+    }
+    voff[i] = o;
+  }
+  const uint16_t* kn_base = a.k_nope + bh * T * DN;
+  const uint16_t* kr_base = a.k_rot + (size_t)b * T * DR;
+  const uint16_t* vt_base = a.v + bh * (size_t)DV * a.v_ld;
+  const uint32_t vt_elems = (uint32_t)DV * (uint32_t)a.v_ld;
+
+  // queue the LDS-direct loads of key tile kt into buffer buf
+  auto issue = [&](int kt, int buf) {
     const int key0 = kt * BN;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kn_base + (size_t)key0 * DN, (uint32_t)(T - key0) * DN * 2u);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(kr_base + (size_t)key0 * DR, (uint32_t)(T - key0) * DR * 2u);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vt_base + key0, (vt_elems - (uint32_t)key0) * 2u);
 #pragma unroll
-    for (int i = 0; i < PER_N; ++i) {
-      const int id = tid + NT * i;
-      const int row = id / (DN / 8), cc = id % (DN / 8);
-      if (NCH_N % NT == 0 || id < NCH_N) kn_reg[i] = buf_load16(rk, (uint32_t)((key0 + row) * DN + cc * 8) * 2);
-    }
-#pragma unroll
-    for (int i = 0; i < PER_R; ++i) {
-      const int id = tid + NT * i;
-      const int row = id / (DR / 8), cc = id % (DR / 8);
-      if (NCH_R % NT == 0 || id < NCH_R) kr_reg[i] = buf_load16(rr, (uint32_t)((key0 + row) * DR + cc * 8) * 2);
-    }
-    // V units: 4 consecutive keys x 8 value columns; the key quad varies
-    // fastest across lanes so the transposed 8-byte LDS stores spread over
-    // the banks
-#pragma unroll
-    for (int i = 0; i < VPER; ++i) {
-      const int u = tid + NT * i;
-      const int kq = u % (BN / 4), dc = u / (BN / 4);
-      if (VUNITS % NT == 0 || u < VUNITS) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v_reg[i][j] = buf_load16(rv, (uint32_t)((key0 + kq * 4 + j) * DV + dc * 8) * 2);
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PER_N; ++i) {
-      const int id = tid + NT * i;
-      const int row = id / (DN / 8), cc = id % (DN / 8);
-      if (NCH_N % NT == 0 || id < NCH_N) *reinterpret_cast<u32x4*>(&sK[buf][row * LDQ + cc * 8]) = kn_reg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < PER_R; ++i) {
-      const int id = tid + NT * i;
-      const int row = id / (DR / 8), cc = id % (DR / 8);
-      if (NCH_R % NT == 0 || id < NCH_R) *reinterpret_cast<u32x4*>(&sK[buf][row * LDQ + DN + cc * 8]) = kr_reg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPER; ++i) {
-      const int u = tid + NT * i;
-      const int kq = u % (BN / 4), dc = u / (BN / 4);
-      if (VUNITS % NT == 0 || u < VUNITS) {
-        // transpose 4 keys x 8 values into 8 rows of 4 keys: one byte
-        // permute per 32-bit word (selector 0x05040100 joins the low halves
-        // of two words, 0x07060302 the high halves)
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const u32x2 lo = {__builtin_amdgcn_perm(v_reg[i][1][e2], v_reg[i][0][e2], 0x05040100u),
-                            __builtin_amdgcn_perm(v_reg[i][3][e2], v_reg[i][2][e2], 0x05040100u)};
-          const u32x2 hi = {__builtin_amdgcn_perm(v_reg[i][1][e2], v_reg[i][0][e2], 0x07060302u),
-                            __builtin_amdgcn_perm(v_reg[i][3][e2], v_reg[i][2][e2], 0x07060302u)};
-          *reinterpret_cast<u32x2*>(&sV[buf][(dc * 8 + 2 * e2) * LDV + kq * 4]) = lo;
-          *reinterpret_cast<u32x2*>(&sV[buf][(dc * 8 + 2 * e2 + 1) * LDV + kq * 4]) = hi;
-        }
+    for (int i = 0; i < LPW; ++i) {
+      const int bi = wave + NW * i;
+      if (bi < NBLK) {
+        void* dst = &smem[buf][bi * 64];
+        if (bi >= KBLK)
+          load_lds16(rv, dst, voff[i]);
+        else if (16 * (bi % QC) < DN)
+          load_lds16(rk, dst, voff[i]);
+        else
+          load_lds16(rr, dst, voff[i]);
       }
     }
   };
@@ -238,26 +233,22 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
 #pragma unroll
   for (int r = 0; r < 16; ++r) negm[r] = 0.f;
 
-  // K row fed by this lane for the S^T MFMA: the permutation that makes the
-  // lane's registers 8*(r>>3) .. hold consecutive keys
-  const int krow = 16 * ((l32 >> 3) >> 1) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
-
-  gload(0);
-  lstore(0);
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nkt) gload(kt + 1);
+    if (kt + 1 < nkt) issue(kt + 1, cur ^ 1);
     const int key0 = kt * BN;
     if (key0 <= qlo + 31) {  // some key of the tile is visible to this wave
+      const u32x4* blk = &smem[cur][lane];
       // S^T = K Q^T, relative to the reference
       f32x16 sacc[NSUB];
 #pragma unroll
       for (int j = 0; j < NSUB; ++j) {
-        const uint16_t* kr = &sK[cur][(j * 32 + krow) * LDQ + 8 * g];
         u32x4 kf[QC];
 #pragma unroll
-        for (int c = 0; c < QC; ++c) kf[c] = *reinterpret_cast<const u32x4*>(kr + 16 * c);
+        for (int c = 0; c < QC; ++c) kf[c] = blk[(j * QC + c) * 64];
         __builtin_amdgcn_sched_barrier(0);
         sacc[j] = ET::mma(kf[0], qf[0], negm);
 #pragma unroll
@@ -279,18 +270,43 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
             if (key > tq) sacc[j][r] = -INFINITY;
           }
       }
-      // tile maximum relative to the reference; move the reference to it on
-      // the first tile and whenever a score exceeds it by more than the slack
-      float mx = -INFINITY;
+      // P = 2^(s - m_ref) as 16-bit B operands (8 consecutive keys per lane)
+      // and this lane's sum of the tile's P
+      u32x4 pf[NPV];
+      auto make_p = [&]() {
+        float ts = 0.f;
 #pragma unroll
-      for (int j = 0; j < NSUB; ++j)
+        for (int m = 0; m < NPV; ++m) {
+          u32x4 pk;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[j][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const bool raise = !ref_set || mx > kRescaleSlack;
-      if (__any(raise)) {
-        // the first tile always holds key 0, visible to every row, so mx is
-        // finite wherever the reference is still unset
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const float p0 = __builtin_amdgcn_exp2f(sacc[m >> 1][8 * (m & 1) + 2 * e2]);
+            const float p1 = __builtin_amdgcn_exp2f(sacc[m >> 1][8 * (m & 1) + 2 * e2 + 1]);
+            pk[e2] = ET::pack2(p0, p1);
+            ts = ET::sum2(pk[e2], ts);
+          }
+          pf[m] = pk;
+        }
+        return ts;
+      };
+      float ts = 0.f;
+      bool exact = !ref_set;
+      if (!exact) {
+        ts = make_p();
+        exact = __any(ts > kSumLimit);
+      }
+      if (exact) {
+        // tile maximum relative to the reference; move the reference to it on
+        // the first tile and wherever a score exceeds it by more than the
+        // slack (the first tile always holds key 0, visible to every row, so
+        // the maximum is finite wherever the reference is still unset)
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NSUB; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[j][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const bool raise = !ref_set || mx > kRescaleSlack;
         const float shift = raise ? mx : 0.f;
         const float alpha = (raise && ref_set) ? __builtin_amdgcn_exp2f(-mx) : 1.f;
         m_ref += shift;
@@ -308,31 +324,19 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
 #pragma unroll
           for (int r = 0; r < 16; ++r) negm[r] = -m_ref;
         }
+        ts = make_p();
       }
-      // P = 2^(s - m_ref) as 16-bit B operands, 8 consecutive keys per lane
-      u32x4 pf[NPV];
-#pragma unroll
-      for (int m = 0; m < NPV; ++m) {
-        u32x4 pk;
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const float p0 = __builtin_amdgcn_exp2f(sacc[m >> 1][8 * (m & 1) + 2 * e2]);
-          const float p1 = __builtin_amdgcn_exp2f(sacc[m >> 1][8 * (m & 1) + 2 * e2 + 1]);
-          pk[e2] = ET::pack2(p0, p1);
-          lsum = ET::sum2(pk[e2], lsum);
-        }
-        pf[m] = pk;
-      }
+      lsum += ts;
       // O^T += V^T P^T
 #pragma unroll
       for (int d = 0; d < NO; ++d) {
-        const uint16_t* vr = &sV[cur][(d * 32 + l32) * LDV + 8 * g];
 #pragma unroll
-        for (int m = 0; m < NPV; ++m)
-          oacc[d] = ET::mma(*reinterpret_cast<const u32x4*>(vr + 16 * m), pf[m], oacc[d]);
+        for (int m = 0; m < NPV; ++m) oacc[d] = ET::mma(blk[(KBLK + d * NPV + m) * 64], pf[m], oacc[d]);
       }
     }
-    if (kt + 1 < nkt) lstore(cur ^ 1);
+    // the next tile's loads have landed in LDS and every wave is done with
+    // this tile's buffer
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -357,6 +361,51 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
   }
 }
 
+// Row-major values [B, H, T, Dv] -> V^T [B, H, Dv, v_ld] (columns T..v_ld-1
+// zero). One workgroup per (64 tokens, 64 value columns), looping over b*H+h.
+__global__ void __launch_bounds__(256) transpose_v_kernel(const uint16_t* __restrict__ v, uint16_t* __restrict__ vt,
+                                                           int BH, int T, int Dv, int v_ld, int ny) {
+  constexpr int LD = 64 + 8;  // LDS row stride (16-bit elements)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * LD];
+  const int tid = threadIdx.x;
+  const int t0 = (blockIdx.x / ny) * 64, d0 = (blockIdx.x % ny) * 64;
+  for (int bh = blockIdx.y; bh < BH; bh += gridDim.y) {
+    const uint16_t* src = v + (size_t)bh * T * Dv;
+    uint16_t* dst = vt + (size_t)bh * Dv * v_ld;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int id = tid + 256 * i;
+      const int tok = id >> 3, dc = id & 7;
+      const int t = t0 + tok, d = d0 + dc * 8;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (t < T && d < Dv) x = *reinterpret_cast<const u32x4*>(src + (size_t)t * Dv + d);
+      *reinterpret_cast<u32x4*>(&tile[tok * LD + dc * 8]) = x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int id = tid + 256 * i;
+      const int dr = id >> 3, tc = id & 7;
+      const int d = d0 + dr, t = t0 + tc * 8;
+      if (d < Dv && t < v_ld) {
+        u32x4 y;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2)
+          y[e2] = (uint32_t)tile[(tc * 8 + 2 * e2) * LD + dr] | ((uint32_t)tile[(tc * 8 + 2 * e2 + 1) * LD + dr] << 16);
+        *reinterpret_cast<u32x4*>(dst + (size_t)d * v_ld + t) = y;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_transpose_v(const uint16_t* v, uint16_t* vt, int BH, int T, int Dv, int v_ld, hipStream_t stream) {
+  const int ny = (Dv + 63) / 64;
+  const dim3 grid((unsigned)(((v_ld + 63) / 64) * ny), (unsigned)(BH < 65535 ? BH : 65535));
+  hipLaunchKernelGGL(transpose_v_kernel, grid, dim3(256), 0, stream, v, vt, BH, T, Dv, v_ld, ny);
+  return hipGetLastError();
+}
+
 bool prefill_supported(int Dqk, int Dr, int Dv) {
   return (Dqk == 48 && Dr == 16 && Dv == 32) || (Dqk == 192 && Dr == 64 && Dv == 128) ||
          (Dqk == 256 && Dr == 64 && Dv == 256);
@@ -375,7 +424,7 @@ static hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
 template <class ET>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
   const int Dqk = a.Dn + a.Dr;
-  if (Dqk == 192 && a.Dv == 128) return launch_one<ET, 192, 64, 128, 32, 8, 2>(a, stream);
+  if (Dqk == 192 && a.Dv == 128) return launch_one<ET, 192, 64, 128, 64, 8, 2>(a, stream);
   if (Dqk == 256 && a.Dv == 256) return launch_one<ET, 256, 64, 256, 32, 4, 1>(a, stream);
   if (Dqk == 48 && a.Dv == 32) return launch_one<ET, 48, 16, 32, 64, 4, 2>(a, stream);
   return hipErrorInvalidValue;

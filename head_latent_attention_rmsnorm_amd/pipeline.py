@@ -34,18 +34,19 @@ def build_table(rope: api.RopeParams, n_pos: int, qk_head_dim: int, device="cuda
 class PrefillBuffers:
     c_norm: torch.Tensor
     k_nope: torch.Tensor
-    v: torch.Tensor
+    v: torch.Tensor  # V^T [B, H, Dv, round8(T)]
     out: torch.Tensor
     workspace: Optional[torch.Tensor] = None
 
 
 def alloc_prefill(B, T, H, R, Dn, Dr, Dv, device="cuda", kv_dtype=torch.float16) -> PrefillBuffers:
     """Intermediate buffers; k_nope and v in `kv_dtype` (fp16 by default: same
-    size and MFMA rate as bf16 on gfx950, three more significant bits)."""
+    size and MFMA rate as bf16 on gfx950, three more significant bits). The
+    values are kept transposed (V^T), the layout the attention reads."""
     return PrefillBuffers(
         c_norm=torch.empty((B, T, R), dtype=torch.float32, device=device),
         k_nope=torch.empty((B, H, T, Dn), dtype=kv_dtype, device=device),
-        v=torch.empty((B, H, T, Dv), dtype=kv_dtype, device=device),
+        v=torch.empty((B, H, Dv, api.round8(T)), dtype=kv_dtype, device=device),
         out=torch.empty((B, H, T, Dv), dtype=torch.bfloat16, device=device),
         workspace=torch.empty((((B * T * Dr * 2) + 255) // 256 * 256,), dtype=torch.uint8, device=device),
     )
@@ -61,9 +62,9 @@ def prefill_forward(q, latent, k_pe, gain, W, table: RopeTable, Dn: int, Dv: int
     if bufs is None:
         bufs = alloc_prefill(B, T, H, R, Dn, Dr, Dv, q.device, kv_dtype)
     api.mla_latent_rmsnorm(latent, gain, eps, out=bufs.c_norm)
-    api.mla_kv_expand(bufs.c_norm, W, H, Dn, Dv, k=bufs.k_nope, v=bufs.v)
+    api.mla_kv_expand(bufs.c_norm, W, H, Dn, Dv, k=bufs.k_nope, v=bufs.v, v_layout="cols")
     return api.mla_prefill_attention(q, bufs.k_nope, k_pe, bufs.v, table.cos, table.sin, table.scale, pairing,
-                                     return_lse=return_lse, out=bufs.out, workspace=bufs.workspace)
+                                     return_lse=return_lse, out=bufs.out, workspace=bufs.workspace, v_layout="cols")
 
 
 def decode_step(q, latent, k_pe, gain, W, k_cache, v_cache, seq_len, q_pos, slot: int, table: RopeTable, Dn: int,

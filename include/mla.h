@@ -81,6 +81,16 @@ typedef enum { MLA_PAIR_HALF = 0, MLA_PAIR_INTERLEAVED = 1 } mla_rope_pairing;
  * keys and outputs stay bf16 at the boundary in both modes. */
 typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP16 = 1 } mla_dtype;
 
+/* Layout of the expanded values. ROWS: [B, H, T, Dv], the layout the pages
+ * produce (transpose(1, 2) of the projection, split off after the keys).
+ * COLS: V^T [B, H, Dv, v_ld], keys contiguous per value column, with a row
+ * stride v_ld that is a multiple of 8 and >= the token count; the padding
+ * columns must hold finite values (mla_kv_expand writes zeros there). The
+ * prefill attention multiplies P by V with keys as the reduction dimension,
+ * so it reads V^T directly; given ROWS it first transposes into its
+ * workspace. */
+typedef enum { MLA_V_ROWS = 0, MLA_V_COLS = 1 } mla_v_layout;
+
 /* Rotary parameters [K2-rope, YaRN class and rope_scaling keys]. The YaRN
  * class defaults printed on the page are base 10000, factor 1.0,
  * original_max_pos 4096, beta_fast 32, beta_slow 1, mscale 1,
@@ -152,7 +162,10 @@ mla_status mla_latent_rmsnorm(const mla_bf16* x, const mla_bf16* w, float eps, f
  * Args: c_norm device fp32 [B, T, R] (from mla_latent_rmsnorm); W device
  *   bf16 [H*(Dn+Dv), R]
  *   (nn.Linear weight layout); k device [B, H, Tcap, k_ld] and v device
- *   [B, H, Tcap, Dv], both of element type kv_dtype (mla_dtype);
+ *   [B, H, Tcap, Dv] (v_layout MLA_V_ROWS, v_ld ignored) or V^T
+ *   [B, H, Dv, v_ld] (MLA_V_COLS, v_ld >= Tcap and a multiple of 8; the call
+ *   that writes column Tcap-1 also zeroes columns Tcap..v_ld-1), both of
+ *   element type kv_dtype (mla_dtype);
  *   0 <= t_off, t_off + T <= Tcap;
  *   k_ld >= Dn (>= Dn+Dr in append mode). Append mode only: k_pe device bf16
  *   [B, T, Dr] (not rotated), cos/sin device fp32 [table_len, Dr/2] from
@@ -163,7 +176,8 @@ mla_status mla_latent_rmsnorm(const mla_bf16* x, const mla_bf16* w, float eps, f
  *   MLA_ERR_UNSUPPORTED (kv_dtype), MLA_ERR_HIP. */
 mla_status mla_kv_expand(const float* c_norm, const mla_bf16* W, int32_t B, int32_t T,
                          int32_t R, int32_t H, int32_t Dn, int32_t Dv, uint16_t* k, int32_t k_ld,
-                         uint16_t* v, int32_t Tcap, int32_t t_off, int32_t kv_dtype,
+                         uint16_t* v, int32_t v_layout, int32_t v_ld, int32_t Tcap, int32_t t_off,
+                         int32_t kv_dtype,
                          const mla_bf16* k_pe, const float* cos, const float* sin,
                          int32_t table_len, const int32_t* pos, int32_t Dr, int32_t pairing,
                          hipStream_t stream);
@@ -179,22 +193,27 @@ mla_status mla_kv_expand(const float* c_norm, const mla_bf16* W, int32_t B, int3
  * 16-bit MFMA in kv_dtype with fp32 accumulation: the rotated query and key
  * parts and P are rounded once to kv_dtype.
  * Args: q device bf16 [B, H, T, Dn+Dr] (rotary part not rotated);
- *   k_nope device [B, H, T, Dn] and v device [B, H, T, Dv] of element type
- *   kv_dtype (from mla_kv_expand); k_pe device bf16 [B, T, Dr] (not
- *   rotated); cos/sin device fp32
+ *   k_nope device [B, H, T, Dn] and v device of element type kv_dtype (from
+ *   mla_kv_expand), v either [B, H, T, Dv] (v_layout MLA_V_ROWS, v_ld
+ *   ignored; transposed into the workspace first) or V^T [B, H, Dv, v_ld]
+ *   (MLA_V_COLS, v_ld >= T, a multiple of 8, padding columns finite);
+ *   k_pe device bf16 [B, T, Dr] (not rotated); cos/sin device fp32
  *   [table_len, Dr/2]; pos device int32 [B, T] or NULL (= 0..T-1, which
  *   needs table_len >= T); scale from mla_softmax_scale; out device bf16
  *   [B, H, T, Dv]; lse device fp32 [B, H, T] or NULL (natural-log
  *   log-sum-exp of each row's scaled scores).
- *   workspace: device scratch of *ws_bytes bytes. Pass workspace == NULL with
+ *   workspace: device scratch of *ws_bytes bytes (the rotated rotary keys
+ *   and, for MLA_V_ROWS, the transposed values). Pass workspace == NULL with
  *   ws_bytes != NULL to query the size (*ws_bytes is set, MLA_OK, nothing
  *   launched).
  *   Supported (Dn+Dr, Dv): (48, 32), (192, 128), (256, 256); Dr in
- *   {16, 64}; T >= 0 (0 is a no-op).
+ *   {16, 64}; T >= 0 (0 is a no-op); one (b, h) slice of k_nope and of V^T
+ *   below 2 GiB.
  * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED,
  *   MLA_ERR_ROPE_TYPE, MLA_ERR_WORKSPACE, MLA_ERR_HIP. */
 mla_status mla_prefill_attention(const mla_bf16* q, const uint16_t* k_nope, const mla_bf16* k_pe,
-                                 const uint16_t* v, int32_t kv_dtype, const float* cos,
+                                 const uint16_t* v, int32_t v_layout, int32_t v_ld,
+                                 int32_t kv_dtype, const float* cos,
                                  const float* sin, int32_t table_len, const int32_t* pos,
                                  int32_t B, int32_t H,
                                  int32_t T, int32_t Dn, int32_t Dr, int32_t Dv, float scale,

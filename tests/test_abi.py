@@ -84,8 +84,8 @@ def test_rmsnorm_validation(lib):
 
 
 def expand(lib, **kw):
-    a = dict(c=FAKE, W=FAKE, B=1, T=4, R=512, H=2, Dn=128, Dv=128, k=FAKE, k_ld=128, v=FAKE, Tcap=4, t_off=0,
-             kv_dtype=1, k_pe=None, cos=None, sin=None, table_len=0, pos=None, Dr=0, pairing=0)
+    a = dict(c=FAKE, W=FAKE, B=1, T=4, R=512, H=2, Dn=128, Dv=128, k=FAKE, k_ld=128, v=FAKE, v_layout=0, v_ld=0,
+             Tcap=4, t_off=0, kv_dtype=1, k_pe=None, cos=None, sin=None, table_len=0, pos=None, Dr=0, pairing=0)
     a.update(kw)
     return lib.mla_kv_expand(*a.values(), None)
 
@@ -103,13 +103,18 @@ def test_kv_expand_validation(lib):
     assert expand(lib, k_pe=FAKE, cos=FAKE, sin=FAKE, table_len=4, Dr=64, k_ld=192, pairing=5) == ROPE
     assert expand(lib, k_pe=FAKE, cos=FAKE, sin=FAKE, table_len=2, Dr=64, k_ld=192) == SHAPE  # table too short
     assert expand(lib, kv_dtype=2) == UNSUP
+    # transposed values: row stride >= Tcap and a multiple of 8
+    assert expand(lib, v_layout=1, v_ld=2) == SHAPE
+    assert expand(lib, v_layout=1, v_ld=12) == SHAPE
+    assert expand(lib, v_layout=2, v_ld=8) == SHAPE
     assert expand(lib, B=0) == OK  # empty: no-op
     assert expand(lib, T=0, c=None, k=None) == OK  # empty tensors may have null data
 
 
 def prefill(lib, ws=FAKE, ws_bytes=None, **kw):
-    a = dict(q=FAKE, kn=FAKE, kpe=FAKE, v=FAKE, kv_dtype=1, cos=FAKE, sin=FAKE, table_len=4096, pos=None, B=1, H=64,
-             T=4096, Dn=128, Dr=64, Dv=128, scale=0.13, pairing=0, out=FAKE, lse=None)
+    a = dict(q=FAKE, kn=FAKE, kpe=FAKE, v=FAKE, v_layout=1, v_ld=4096, kv_dtype=1, cos=FAKE, sin=FAKE,
+             table_len=4096, pos=None, B=1, H=64, T=4096, Dn=128, Dr=64, Dv=128, scale=0.13, pairing=0, out=FAKE,
+             lse=None)
     a.update(kw)
     return lib.mla_prefill_attention(*a.values(), ws, ws_bytes, None)
 
@@ -118,6 +123,13 @@ def test_prefill_validation(lib):
     need = ctypes.c_size_t(0)
     assert prefill(lib, ws=None, ws_bytes=ctypes.byref(need)) == OK
     assert need.value == 4096 * 64 * 2
+    # row-major values are transposed into the workspace: [B, H, Dv, round8(T)] more
+    assert prefill(lib, ws=None, ws_bytes=ctypes.byref(need), v_layout=0, T=4095, table_len=4095) == OK
+    assert need.value == (4095 * 64 * 2 + 255) // 256 * 256 + 64 * 128 * 4096 * 2
+    assert prefill(lib, v_ld=4090) == SHAPE  # below T
+    assert prefill(lib, v_ld=4100) == SHAPE  # not a multiple of 8
+    assert prefill(lib, v_layout=3) == SHAPE
+    assert prefill(lib, v_ld=1 << 30) == SHAPE  # one V^T slice beyond 2 GiB
     assert prefill(lib, q=None) == NULL
     assert prefill(lib, Dn=100) == UNSUP
     assert prefill(lib, Dv=64) == UNSUP

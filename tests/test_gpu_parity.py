@@ -113,6 +113,38 @@ def test_kv_expand(s, kv_dtype):
         assert np.all(d <= bound), what
 
 
+@pytest.mark.parametrize("kv_dtype", [torch.float16, torch.bfloat16], ids=["fp16", "bf16"])
+@pytest.mark.parametrize("s", EXPAND_SHAPES, ids=lambda s: "B{B}T{T}H{H}R{R}n{Dn}v{Dv}".format(**s))
+def test_kv_expand_v_cols(s, kv_dtype):
+    """Transposed values (V^T [B, H, Dv, v_ld]) hold exactly the row-major
+    values, and the padding columns are zeroed by the call that writes the
+    last column (in one call, and in two appends)."""
+    say(f"[kv_expand V^T] {s} {kv_dtype}")
+    B, T, H, R, Dn, Dv = (s[x] for x in ("B", "T", "H", "R", "Dn", "Dv"))
+    g = torch.Generator().manual_seed(T * 5 + H)
+    c = torch.randn(B, T, R, generator=g).cuda()
+    Wt = (torch.randn(H * (Dn + Dv), R, generator=g) / math.sqrt(R)).to(torch.bfloat16).cuda()
+    k1, v1 = api.mla_kv_expand(c, Wt, H, Dn, Dv, kv_dtype=kv_dtype)
+    ld = api.round8(T) + 8
+    k2 = torch.empty_like(k1)
+    vt = torch.full((B, H, Dv, ld), float("nan"), dtype=kv_dtype, device="cuda")
+    api.mla_kv_expand(c, Wt, H, Dn, Dv, k=k2, v=vt, v_layout="cols")
+    torch.cuda.synchronize()
+    assert torch.equal(k1, k2)
+    assert torch.equal(vt[..., :T], v1.transpose(2, 3))
+    assert torch.all(vt[..., T:] == 0)
+    if T > 1:
+        t1 = T // 3
+        vt2 = torch.full_like(vt, float("nan"))
+        k3 = torch.empty_like(k1)
+        api.mla_kv_expand(c[:, :t1].contiguous(), Wt, H, Dn, Dv, k=k3, v=vt2, v_layout="cols")
+        torch.cuda.synchronize()
+        assert torch.all(torch.isnan(vt2[..., T:]))  # column T-1 not written yet: padding untouched
+        api.mla_kv_expand(c[:, t1:].contiguous(), Wt, H, Dn, Dv, k=k3, v=vt2, t_off=t1, v_layout="cols")
+        torch.cuda.synchronize()
+        assert torch.equal(vt2, vt) and torch.equal(k3, k1)
+
+
 def test_kv_expand_append_into_cache():
     say("[kv_expand append]")
     w = W_["kimi_k2_decode"]
@@ -242,6 +274,36 @@ def test_prefill_ragged(w, kv_dtype):
     out = run_prefill(w, inp, kv_dtype=kv_dtype)
     assert_close(f64(out), O.prefill(w, inp), f"{w.name} {kv_dtype}",
                  max_abs=MAX_ABS if kv_dtype == torch.float16 else BF16_MAX_ABS)
+
+
+LAYOUT_CASES = [
+    workloads.custom(name="k2", B=2, T=333, H=3, R=512, Dn=128, Dr=64, Dv=128, seed=41, rope=workloads.YARN_KIMI),
+    workloads.custom(name="glm", B=1, T=130, H=2, R=512, Dn=192, Dr=64, Dv=256, seed=42, pairing="interleaved"),
+    workloads.custom(name="tiny", B=2, T=77, H=2, R=64, Dn=32, Dr=16, Dv=32, seed=43),
+]
+
+
+@pytest.mark.parametrize("w", LAYOUT_CASES, ids=lambda w: w.name)
+def test_prefill_v_layouts_agree(w):
+    """Row-major values (transposed inside the call) and V^T give the same
+    bits, and finite garbage in the V^T padding columns changes nothing
+    (those keys are masked, P = 0)."""
+    say(f"[prefill layouts] {w.name} B={w.B} T={w.T}")
+    g = to_gpu(workloads.make_inputs(w))
+    tab = table(w)
+    c = api.mla_latent_rmsnorm(g["latent"], g["gain"], w.eps)
+    kn, v = api.mla_kv_expand(c, g["W"], w.H, w.Dn, w.Dv)
+    _, vt = api.mla_kv_expand(c, g["W"], w.H, w.Dn, w.Dv, v_layout="cols")
+    o_rows = api.mla_prefill_attention(g["q"], kn, g["k_pe"], v, tab.cos, tab.sin, tab.scale, w.pairing)
+    o_cols = api.mla_prefill_attention(g["q"], kn, g["k_pe"], vt, tab.cos, tab.sin, tab.scale, w.pairing,
+                                       v_layout="cols")
+    wide = torch.full((w.B, w.H, w.Dv, api.round8(w.T) + 16), 1000.0, dtype=vt.dtype, device="cuda")
+    wide[..., :w.T] = vt[..., :w.T]
+    o_wide = api.mla_prefill_attention(g["q"], kn, g["k_pe"], wide, tab.cos, tab.sin, tab.scale, w.pairing,
+                                       v_layout="cols")
+    torch.cuda.synchronize()
+    assert torch.equal(o_rows, o_cols)
+    assert torch.equal(o_rows, o_wide)
 
 
 def test_prefill_bf16_mode_kimi_1k():
