@@ -32,16 +32,20 @@
 //    O^T = V^T P^T with no data movement;
 //  - all K fragments of a sub-tile are read from LDS before its MFMAs start
 //    (a scheduling fence keeps them in flight together);
+//  - each 64-key tile is software-pipelined over its two 32-key sub-tiles:
+//    the score MFMAs of sub-tile 1 are issued ahead of the softmax of
+//    sub-tile 0, and the PV MFMAs of sub-tile 0 ahead of the softmax of
+//    sub-tile 1;
 //  - MFMA and VALU work hardly overlap on this chip, so the softmax is cut to
 //    the bone: in fp16 mode the query is pre-scaled by scale*log2(e) and the
 //    first MFMA of every score chain accumulates onto -m (the running
 //    reference maximum), so the scores leave the MFMA as exp2 arguments. The
-//    reference only moves when this tile's P would leave a safe range: the
-//    per-lane sum of the tile's P (taken anyway, with v_dot2 on the packed
-//    16-bit P that the PV product consumes) bounds every P, and only when it
-//    exceeds 2^14 (or on the first tile) is the exact tile maximum taken and
-//    the reference raised to it (exact: O and the row sum share the
-//    reference);
+//    reference only moves when a sub-tile's P would leave a safe range: the
+//    per-lane sum of the sub-tile's P (taken anyway, with v_dot2 on the
+//    packed 16-bit P that the PV product consumes) bounds every P, and only
+//    when it exceeds 2^14 (or on the first sub-tile) is the exact maximum
+//    taken and the reference raised to it (exact: O and the row sum share
+//    the reference);
 //  - only the tiles crossing a wave's diagonal are masked; tiles above it are
 //    neither loaded nor multiplied;
 //  - workgroup ids are dealt to the 8 XCDs round-robin; the id -> (b, h,
@@ -102,9 +106,11 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
 
   const int l32 = lane & 31;
   const int g = lane >> 5;
-  const int rb = (NW == 8 && wave >= 4) ? 11 - wave : wave;  // row block of this wave
-  const int qlo = qt * BMW + rb * 32;  // first query row of this wave
-  const int tq = qlo + l32;            // this lane's query row
+  // 32-row block of this wave; with 8 waves the blocks are dealt so that the
+  // waves sharing a SIMD (w and w+4) get blocks s and 7-s, which evens out
+  // the triangular work of the diagonal tiles
+  const int qlo = qt * BMW + ((NW == 8 && wave >= 4) ? 11 - wave : wave) * 32;
+  const int tq = qlo + l32;  // this lane's query row
   const float sl2 = a.scale * kLog2e;
   const float qmul = FOLD ? sl2 : 1.0f;  // query pre-scale
 
@@ -199,7 +205,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
   const uint32_t vt_elems = (uint32_t)DV * (uint32_t)a.v_ld;
 
   // queue the LDS-direct loads of key tile kt into buffer buf
-  auto issue = [&](int kt, int buf) {
+  auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
     const int key0 = kt * BN;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kn_base + (size_t)key0 * DN, (uint32_t)(T - key0) * DN * 2u);
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(kr_base + (size_t)key0 * DR, (uint32_t)(T - key0) * DR * 2u);
@@ -225,86 +231,79 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
 #pragma unroll
   for (int d = 0; d < NO; ++d)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
+    for (int i = 0; i < 16; ++i) oacc[d][i] = 0.f;
   float m_ref = 0.f;
   bool ref_set = false;
   float lsum = 0.f;  // this lane's share of the row sum
   f32x16 negm;       // -m_ref broadcast: the initial score accumulator
 #pragma unroll
-  for (int r = 0; r < 16; ++r) negm[r] = 0.f;
+  for (int i = 0; i < 16; ++i) negm[i] = 0.f;
 
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nkt) issue(kt + 1, cur ^ 1);
-    const int key0 = kt * BN;
-    if (key0 <= qlo + 31) {  // some key of the tile is visible to this wave
-      const u32x4* blk = &smem[cur][lane];
-      // S^T = K Q^T, relative to the reference
-      f32x16 sacc[NSUB];
+  // One key tile, software-pipelined over its 32-key sub-tiles: the score
+  // MFMAs of sub-tile j+1 are issued before the softmax of sub-tile j, and
+  // the PV MFMAs of sub-tile j before the softmax of j+1, so the exp and
+  // conversion work of one sub-tile can run under the MFMAs of another.
+  auto tile = [&](int cur, int key0) __attribute__((always_inline)) {
+    const u32x4* blk = &smem[cur][lane];
+    const bool diag = key0 + BN - 1 > qlo;  // the tile crosses the wave's diagonal
+    f32x16 sacc[NSUB];
+    u32x4 pf[NPV];
+    auto s_chain = [&](int j) __attribute__((always_inline)) {
+      u32x4 kf[QC];
 #pragma unroll
-      for (int j = 0; j < NSUB; ++j) {
-        u32x4 kf[QC];
+      for (int c = 0; c < QC; ++c) kf[c] = blk[(j * QC + c) * 64];
+      __builtin_amdgcn_sched_barrier(0);
+      sacc[j] = ET::mma(kf[0], qf[0], negm);
 #pragma unroll
-        for (int c = 0; c < QC; ++c) kf[c] = blk[(j * QC + c) * 64];
-        __builtin_amdgcn_sched_barrier(0);
-        sacc[j] = ET::mma(kf[0], qf[0], negm);
-#pragma unroll
-        for (int c = 1; c < QC; ++c) sacc[j] = ET::mma(kf[c], qf[c], sacc[j]);
-      }
+      for (int c = 1; c < QC; ++c) sacc[j] = ET::mma(kf[c], qf[c], sacc[j]);
+    };
+    // scale (bf16 mode) and mask the scores of sub-tile j
+    auto finish = [&](int j) __attribute__((always_inline)) {
       if (!FOLD) {
 #pragma unroll
-        for (int j = 0; j < NSUB; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[j][r] = fmaf(sacc[j][r], sl2, -m_ref);
+        for (int i = 0; i < 16; ++i) sacc[j][i] = fmaf(sacc[j][i], sl2, -m_ref);
       }
-      // causal mask on the tiles that cross the diagonal
-      if (key0 + BN - 1 > qlo) {
+      if (diag) {
 #pragma unroll
-        for (int j = 0; j < NSUB; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + j * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
-            if (key > tq) sacc[j][r] = -INFINITY;
-          }
-      }
-      // P = 2^(s - m_ref) as 16-bit B operands (8 consecutive keys per lane)
-      // and this lane's sum of the tile's P
-      u32x4 pf[NPV];
-      auto make_p = [&]() {
-        float ts = 0.f;
-#pragma unroll
-        for (int m = 0; m < NPV; ++m) {
-          u32x4 pk;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const float p0 = __builtin_amdgcn_exp2f(sacc[m >> 1][8 * (m & 1) + 2 * e2]);
-            const float p1 = __builtin_amdgcn_exp2f(sacc[m >> 1][8 * (m & 1) + 2 * e2 + 1]);
-            pk[e2] = ET::pack2(p0, p1);
-            ts = ET::sum2(pk[e2], ts);
-          }
-          pf[m] = pk;
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + j * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
+          if (key > tq) sacc[j][i] = -INFINITY;
         }
-        return ts;
-      };
-      float ts = 0.f;
-      bool exact = !ref_set;
-      if (!exact) {
-        ts = make_p();
-        exact = __any(ts > kSumLimit);
       }
-      if (exact) {
-        // tile maximum relative to the reference; move the reference to it on
-        // the first tile and wherever a score exceeds it by more than the
-        // slack (the first tile always holds key 0, visible to every row, so
-        // the maximum is finite wherever the reference is still unset)
+    };
+    // P = 2^(s - m_ref) of sub-tile j as 16-bit B operands (8 consecutive
+    // keys per lane) and this lane's sum of them
+    auto make_p = [&](int j) __attribute__((always_inline)) {
+      float t = 0.f;
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        u32x4 pk;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float p0 = __builtin_amdgcn_exp2f(sacc[j][8 * mm + 2 * e2]);
+          const float p1 = __builtin_amdgcn_exp2f(sacc[j][8 * mm + 2 * e2 + 1]);
+          pk[e2] = ET::pack2(p0, p1);
+          t = ET::sum2(pk[e2], t);
+        }
+        pf[2 * j + mm] = pk;
+      }
+      return t;
+    };
+    s_chain(0);
+    finish(0);
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) {
+      if (j + 1 < NSUB) s_chain(j + 1);
+      float ts = make_p(j);
+      if (__any(!ref_set || ts > kSumLimit)) {
+        // the exact maximum of the sub-tile (relative to the reference);
+        // move the reference to it on the first sub-tile and wherever a
+        // score exceeds it by more than the slack (the first sub-tile holds
+        // key 0, visible to every row, so the maximum is finite where the
+        // reference is still unset)
         float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < NSUB; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[j][r]);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[j][i]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const bool raise = !ref_set || mx > kRescaleSlack;
         const float shift = raise ? mx : 0.f;
@@ -315,25 +314,39 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
 #pragma unroll
         for (int d = 0; d < NO; ++d)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+          for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
 #pragma unroll
-        for (int j = 0; j < NSUB; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[j][r] -= shift;
+        for (int i = 0; i < 16; ++i) sacc[j][i] -= shift;
         if (FOLD) {
+          // the next sub-tile's scores were accumulated onto the old -m_ref
+          if (j + 1 < NSUB) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) negm[r] = -m_ref;
+            for (int i = 0; i < 16; ++i) sacc[j + 1][i] -= shift;
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) negm[i] = -m_ref;
         }
-        ts = make_p();
+        ts = make_p(j);
       }
       lsum += ts;
-      // O^T += V^T P^T
+      if (j + 1 < NSUB) finish(j + 1);
+      // O^T += V^T P^T over the sub-tile's two 16-key steps
 #pragma unroll
-      for (int d = 0; d < NO; ++d) {
+      for (int d = 0; d < NO; ++d)
 #pragma unroll
-        for (int m = 0; m < NPV; ++m) oacc[d] = ET::mma(blk[(KBLK + d * NPV + m) * 64], pf[m], oacc[d]);
-      }
+        for (int mm = 0; mm < 2; ++mm)
+          oacc[d] = ET::mma(blk[(KBLK + d * NPV + 2 * j + mm) * 64], pf[2 * j + mm], oacc[d]);
     }
+  };
+
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nkt) issue(kt + 1, cur ^ 1);
+    const int key0 = kt * BN;
+    if (key0 <= qlo + 31) tile(cur, key0);  // some key of the tile is visible to this wave
     // the next tile's loads have landed in LDS and every wave is done with
     // this tile's buffer
     __builtin_amdgcn_s_waitcnt(0);
