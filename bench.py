@@ -146,7 +146,7 @@ def main():
     bufs = mla.pipeline.alloc_prefill(wp.B, wp.T, wp.H, wp.R, wp.Dn, wp.Dr, wp.Dv, dev)
     seq = torch.full((wd.B,), wd.cache_len, dtype=torch.int32, device=dev)
     qpos = torch.full((wd.B,), wd.q_pos, dtype=torch.int32, device=dev)
-    c_dec = torch.empty((wd.B, 1, wd.R), dtype=torch.float32, device=dev)
+    c_dec = torch.empty((wd.B, 1, wd.R), dtype=torch.float16, device=dev)
     out_dec = torch.empty((wd.B, wd.H, 1, wd.Dv), dtype=torch.bfloat16, device=dev)
     splits = args.splits or 0
     ws_dec = torch.empty((max(1, 64 << 20),), dtype=torch.uint8, device=dev)

@@ -101,14 +101,14 @@ def mla_rope_table_build(rope: RopeParams, n_pos: int, device="cuda") -> Tuple[t
 def mla_latent_rmsnorm(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """RMSNorm over the last dim of x (bf16 [..., R]) with weight w (bf16 [R]);
-    returns the normalised latent in fp32 [..., R]."""
+    returns the normalised latent in fp16 [..., R]."""
     _need(x, "x")
     _need(w, "w")
     R = x.shape[-1]
     if w.numel() != R:
         raise ValueError("weight size does not match the latent width")
-    y = torch.empty(x.shape, dtype=torch.float32, device=x.device) if out is None else out
-    _need(y, "out", torch.float32)
+    y = torch.empty(x.shape, dtype=torch.float16, device=x.device) if out is None else out
+    _need(y, "out", torch.float16)
     _shape(y, "out", x.shape)
     n = x.numel() // R if R else 0
     check("mla_latent_rmsnorm",
@@ -133,7 +133,7 @@ def mla_kv_expand(c_norm: torch.Tensor, W: torch.Tensor, H: int, Dn: int, Dv: in
                   k_pe: Optional[torch.Tensor] = None, cos: Optional[torch.Tensor] = None,
                   sin: Optional[torch.Tensor] = None, pos: Optional[torch.Tensor] = None,
                   pairing="half", kv_dtype=torch.float16, v_layout: str = "rows") -> Tuple[torch.Tensor, torch.Tensor]:
-    """kv_b_proj of c_norm (fp32 [B, T, R]) by W (bf16 [H*(Dn+Dv), R]).
+    """kv_b_proj of c_norm (fp16 [B, T, R]) by W (bf16 [H*(Dn+Dv), R]).
 
     Without k/v: returns new k_nope [B, H, T, Dn] and v, [B, H, T, Dv] for
     v_layout "rows" or V^T [B, H, Dv, round8(T)] for "cols" (padding columns
@@ -142,7 +142,7 @@ def mla_kv_expand(c_norm: torch.Tensor, W: torch.Tensor, H: int, Dn: int, Dv: in
     With k [B, H, Tcap, k_ld] and v [B, H, Tcap, Dv] (or V^T [B, H, Dv, v_ld]):
     writes rows (columns) t_off .. t_off+T-1; with k_pe [B, T, Dr] also writes
     the rotated shared key into k[..., Dn:Dn+Dr] of every head (append mode)."""
-    _need(c_norm, "c_norm", torch.float32)
+    _need(c_norm, "c_norm", torch.float16)
     _need(W, "W")
     lcode = _layout_code(v_layout)
     B, T, R = c_norm.shape

@@ -117,7 +117,7 @@ mla_status mla_rope_table_build(const mla_rope_params* p, int32_t n_pos, float* 
   return hip_status(mla::launch_rope_table(r, n_pos, cos_out, sin_out, stream));
 }
 
-mla_status mla_latent_rmsnorm(const mla_bf16* x, const mla_bf16* w, float eps, float* y, int32_t n, int32_t R,
+mla_status mla_latent_rmsnorm(const mla_bf16* x, const mla_bf16* w, float eps, uint16_t* y, int32_t n, int32_t R,
                               hipStream_t stream) {
   if (n < 0 || R < 1 || R > 8192 || !(eps >= 0.0f) || !isfinite(eps)) return MLA_ERR_SHAPE;
   if ((int64_t)n * R > kMaxElems) return MLA_ERR_SHAPE;
@@ -127,7 +127,7 @@ mla_status mla_latent_rmsnorm(const mla_bf16* x, const mla_bf16* w, float eps, f
   return hip_status(mla::launch_rmsnorm(x, w, eps, y, n, R, stream));
 }
 
-mla_status mla_kv_expand(const float* c_norm, const mla_bf16* W, int32_t B, int32_t T, int32_t R, int32_t H,
+mla_status mla_kv_expand(const uint16_t* c_norm, const mla_bf16* W, int32_t B, int32_t T, int32_t R, int32_t H,
                          int32_t Dn, int32_t Dv, uint16_t* k, int32_t k_ld, uint16_t* v, int32_t v_layout,
                          int32_t v_ld, int32_t Tcap, int32_t t_off, int32_t kv_dtype, const mla_bf16* k_pe,
                          const float* cos, const float* sin, int32_t table_len, const int32_t* pos, int32_t Dr,

@@ -3,76 +3,386 @@
 // normalised latent, viewed [B, T, H, Dn+Dv], moved head-major and split into
 // k_nope and value; GLM-5 "Normalized key-value latent", expand_kv).
 //
-// GEMM C^T[n][tok] = W[n][:] . c[tok][:] on bf16 MFMA 32x32x16 with fp32
-// accumulation. The normalised latent arrives in fp32 and is split on its way
-// into LDS into hi = bf16(c) and lo = bf16(c - hi); every W fragment is
-// multiplied by both, so the latent enters the product to 16 significant bits
-// and the only bf16 rounding left is the one of each output. Both operands
-// are K-contiguous (nn.Linear weight [N, R] and latent [M, R]), so each lane
-// feeds the MFMA with one 16-byte LDS read per operand. Computing C^T puts
-// four consecutive output columns n in one lane, which the epilogue packs
-// into one 8-byte store straight into the head-major k_nope / v layout (a
-// 4-column group never straddles a head or the k/v boundary because Dn and Dv
-// are multiples of 8).
+// GEMM kv[tok][n] = sum_r c[tok][r] W[n][r] on fp16 MFMA 32x32x16 with fp32
+// accumulation: the normalised latent arrives in fp16, and W (bf16) is
+// widened to fp16 on its way into LDS, which is exact for every bf16 value of
+// magnitude >= 2^-24 (smaller ones contribute below fp32 resolution of the
+// sum). Both operands are K-contiguous (latent [M, R] and nn.Linear weight
+// [N, R]), so each MFMA operand is one 16-byte run of a row. Each output
+// column n is one element of head h = n / (Dn+Dv): a key element when
+// n mod (Dn+Dv) < Dn, else a value element; the epilogue writes it straight
+// into the head-major k_nope / v (or V^T) layout.
 //
-// With v_cols set, values are written transposed (V^T [B, H, Dv, v_ld], the
-// layout the prefill attention reads): one 2-byte store per value, 32
-// consecutive tokens per store instruction.
-//
-// Workgroup tile 128 n x 128 tokens, 4 waves in 2x2, each 64 x 64 (2x2 MFMA
-// tiles); K staged 32 at a time, double-buffered in LDS with a 16-byte row
-// pad; global loads for stage s+1 are in flight while stage s is multiplied.
+// Two kernels:
+//  - expand_tile_kernel: 256 tokens x 256 columns per workgroup, 8 waves of
+//    128 tokens x 64 columns, launched once over the key columns of all heads
+//    and once over the value columns (Dn and Dv multiples of 64). The latent
+//    tiles move global -> LDS with 16-byte LDS-direct buffer loads gathered
+//    into MFMA fragment order; W tiles go through registers for the fp16
+//    widening and land in the same fragment order; both double-buffered over
+//    the reduction. The value launch with V^T output computes C = c W^T (a
+//    lane then holds four consecutive tokens of one value column: one 8-byte
+//    store into a V^T row); the others compute C^T = W c^T (four consecutive
+//    columns of one token: one 8-byte store into a k_nope / v row). Swapping
+//    the two MFMA operands is all it takes: an A and a B fragment have the
+//    same lane layout.
+//  - expand_small_kernel: 128 columns x 128 tokens, 4 waves, everything staged
+//    through registers; any shape (used for few tokens, e.g. the decode
+//    append, and head widths that are not multiples of 64).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mla {
 
 namespace {
-constexpr int TN = 128;       // W rows (output columns) per workgroup
-constexpr int TM = 128;       // tokens per workgroup
-constexpr int BK = 32;        // reduction depth per LDS stage
-constexpr int LDK = BK + 8;   // LDS row stride (bf16 elements), 16-byte pad
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 8 bf16 (one 16-byte chunk) widened to 8 fp16
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w) {
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = pack2h(__uint_as_float(w[e] << 16), __uint_as_float(w[e] & 0xffff0000u));
+  return o;
+}
+
+__device__ __forceinline__ f32x16 mma16(u32x4 a, u32x4 b, f32x16 c) { return F16::mma(a, b, c); }
+
+// Destination of output column n (global) of token tok: k or v element.
+struct ColInfo {
+  int h, c;   // head and column within the head's Dn+Dv
+  bool is_v;
+};
+__device__ __forceinline__ ColInfo col_info(const ExpandArgs& a, int n) {
+  const int DnDv = a.Dn + a.Dv;
+  ColInfo ci;
+  ci.h = n / DnDv;
+  ci.c = n - ci.h * DnDv;
+  ci.is_v = ci.c >= a.Dn;
+  return ci;
+}
+
+// Store four consecutive columns n..n+3 (same head, same k/v part) of token
+// tok into a row-major k_nope or v row.
+template <class ET>
+__device__ __forceinline__ void store_row4(const ExpandArgs& a, int tok, int n, float x0, float x1, float x2,
+                                           float x3) {
+  const ColInfo ci = col_info(a, n);
+  const int b = tok / a.T;
+  const int t = tok - b * a.T;
+  const size_t rowi = ((size_t)b * a.H + ci.h) * a.Tcap + a.t_off + t;
+  uint16_t* dst = ci.is_v ? a.v + rowi * a.Dv + (ci.c - a.Dn) : a.k + rowi * a.k_ld + ci.c;
+  u32x2 o;
+  o[0] = ET::pack2(x0, x1);
+  o[1] = ET::pack2(x2, x3);
+  *reinterpret_cast<u32x2*>(dst) = o;
+}
+
+// Store value column n of token tok into V^T; the write of the cache's last
+// column also zeroes the row padding.
+template <class ET>
+__device__ __forceinline__ void store_vt1(const ExpandArgs& a, int tok, int n, float x) {
+  const ColInfo ci = col_info(a, n);
+  const int b = tok / a.T;
+  const int t = tok - b * a.T;
+  const int col = a.t_off + t;
+  uint16_t* dst = a.v + (((size_t)b * a.H + ci.h) * a.Dv + (ci.c - a.Dn)) * a.v_ld + col;
+  dst[0] = ET::enc(x);
+  if (col == a.Tcap - 1) {
+#pragma unroll 1
+    for (int z = col + 1; z < a.v_ld; ++z) dst[z - col] = 0;
+  }
+}
+}  // namespace
+
+// ---------------------------------------------------------------- tile kernel
+namespace {
+constexpr int XT_M = 256;  // tokens per workgroup
+constexpr int XT_N = 256;  // columns per workgroup
+constexpr int XT_K = 32;   // reduction depth per stage
+constexpr int XT_NB = 4;   // stages in flight (LDS buffers); loads run XT_NB-1 stages ahead
+constexpr int XT_R = 512;  // latent width the tile kernel is built for (fully unrolled stages)
+}  // namespace
+
+// One part of the columns: the key columns of every head (VPART false: H*Dn
+// columns, written to k_nope rows) or the value columns (VPART true: H*Dv
+// columns, written to v rows, or to V^T when COLS). Part column n belongs to
+// head n / D (D = Dn or Dv) and is row h*(Dn+Dv) + (VPART ? Dn : 0) + n % D
+// of W.
+template <class ET, bool VPART, bool COLS>
+__global__ void __launch_bounds__(512, 2) expand_tile_kernel(ExpandArgs a, int M) {
+  constexpr int KS = XT_K / 16;              // 16-deep MFMA steps per stage
+  constexpr int XT_BLK = (XT_M / 32) * KS;   // 1 KB fragment blocks per operand per stage
+  constexpr int APW = XT_BLK / 8;            // latent LDS-direct loads per wave per stage
+  constexpr int WPT = XT_N * XT_K / 8 / 512; // W 16-byte chunks per thread per stage
+  // [stage buffer][A blocks | B blocks], each block 64 lanes x 16 bytes
+  __shared__ __attribute__((aligned(16))) u32x4 smem[XT_NB][2 * XT_BLK * 64];
+
+  const int D = VPART ? a.Dv : a.Dn;
+  const int N = a.H * D;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2;  // 128-token half of the tile
+  const int wn = wave & 3;   // 64-column quarter
+  const int l32 = lane & 31, g = lane >> 5;
+  const int n0 = blockIdx.x * XT_N;
+  const int m0 = blockIdx.y * XT_M;
+  constexpr int R = XT_R;
+  constexpr int nstage = R / XT_K;
+
+  // latent: LDS-direct loads, APW blocks per wave per stage; block bi =
+  // (m-tile bi/KS, k-step bi%KS), lane = (row l32, 8 columns at 8g); rows
+  // past the last token read as zeros
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.c + (size_t)m0 * R, (uint32_t)(M - m0) * (uint32_t)R * 2u);
+  uint32_t voff[APW];
+#pragma unroll
+  for (int i = 0; i < APW; ++i) {
+    const int bi = wave + 8 * i;
+    voff[i] = (uint32_t)(((bi / KS) * 32 + l32) * R + (bi % KS) * 16 + 8 * g) * 2u;
+  }
+  auto issue_a = [&](int s, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < APW; ++i) {
+      const int bi = wave + 8 * i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)&smem[buf][bi * 64], 16, voff[i], s * XT_K * 2, 0, 0);
+    }
+  };
+  // W: WPT 16-byte chunks per thread per stage, chunk id = tid + 512j: part
+  // column n0 + id/(XT_K/8), 8 reduction elements at 8*(id%(XT_K/8));
+  // widened in registers and stored at its fragment slot
+  constexpr int CPR = XT_K / 8;  // chunks per W row per stage
+  // (columns past the part are read from W row 0: their products only feed
+  // waves that store nothing, and every thread issues the same loads, which
+  // the vmcnt bookkeeping below relies on)
+  const uint16_t* wrow[WPT];
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    const int n = n0 + (tid + 512 * j) / CPR;
+    const int h = n / D;
+    const size_t row = n < N ? (size_t)h * (a.Dn + a.Dv) + (VPART ? a.Dn : 0) + (n - h * D) : 0;
+    wrow[j] = a.W + row * R + ((tid + 512 * j) % CPR) * 8;
+  }
+  // W chunks of the stages in flight are held in registers, one set per
+  // stage buffer (the stage loop is unrolled by XT_NB so the set is static)
+  u32x4 wreg[XT_NB][WPT];
+  auto load_w = [&](int s, int set) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) wreg[set][j] = *reinterpret_cast<const u32x4*>(wrow[j] + s * XT_K);
+  };
+  auto store_w = [&](int set) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const int id = tid + 512 * j;
+      const int nl = id / CPR, kc = id % CPR;
+      const int blk = XT_BLK + (nl >> 5) * KS + (kc >> 1);
+      smem[set][blk * 64 + (nl & 31) + 32 * (kc & 1)] = bf16x8_to_f16x8(wreg[set][j]);
+    }
+  };
+
+  const int nw = n0 + wn * 64;  // this wave's first part column
+  const bool active = nw < N;
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // vector-memory operations per wave per stage (LDS-direct latent loads and
+  // W loads); s_waitcnt vmcnt(n) with n = this times the number of younger
+  // stages in flight waits exactly for the oldest stage
+  constexpr int PER = APW + WPT;
+  static_assert(2 * PER <= 15, "vmcnt field");
+#pragma unroll
+  for (int u = 0; u < XT_NB - 1; ++u) {
+    if (u < nstage) {
+      issue_a(u, u);
+      load_w(u, u);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  store_w(0);
+  __syncthreads();
+#pragma unroll
+  for (int s0 = 0; s0 < nstage; s0 += XT_NB) {
+#pragma unroll
+    for (int u = 0; u < XT_NB; ++u) {
+    const int s = s0 + u;  // stage s lives in buffer / register set u
+    if (s + XT_NB - 1 < nstage) {
+      issue_a(s + XT_NB - 1, (u + XT_NB - 1) % XT_NB);
+      load_w(s + XT_NB - 1, (u + XT_NB - 1) % XT_NB);
+    }
+    if (active) {
+      const u32x4* blk = &smem[u][lane];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 fa[4], fb[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = blk[((wm * 4 + i) * KS + ks) * 64];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb[j] = blk[(XT_BLK + (wn * 2 + j) * KS + ks) * 64];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = COLS ? mma16(fa[i], fb[j], acc[i][j]) : mma16(fb[j], fa[i], acc[i][j]);
+      }
+    }
+    if (s + 1 < nstage) {
+      // stage s+1 has landed (its latent in LDS, its W in registers), the
+      // younger stages may still be in flight
+      if (s + 3 < nstage)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * PER));
+      else if (s + 2 < nstage)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | PER);
+      else
+        __builtin_amdgcn_s_waitcnt(0);
+      store_w((u + 1) % XT_NB);
+    }
+    // workgroup barrier without the fence __syncthreads() carries: that fence
+    // would also wait for the LDS-direct loads of the younger stages. The
+    // waits above cover stage s+1's loads; this one the LDS stores of its W.
+    // The empty asm statements keep the compiler from moving LDS accesses
+    // across the barrier.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    }
+  }
+  if (!active) return;
+
+  // epilogue, staged through LDS (free after the last stage's barrier) so that
+  // every global store writes whole row segments: the wave's 128 x 64 output
+  // tile takes exactly its 16 KB share of LDS, unpadded; the 16-byte chunks of
+  // a tile row are XOR-swizzled with the row index to spread the banks. The
+  // wave's 64 columns belong to one head (D is a multiple of 64).
+  const int h = nw / D;
+  const int cw = nw - h * D;  // the wave's first column within the head's k or v part
+  const int tw = m0 + wm * 128;  // the wave's first token
+  uint16_t* stile = reinterpret_cast<uint16_t*>(&smem[0][0]) + wave * (16384 / 2);
+  if (!COLS) {
+    // C^T tiles: lane holds columns (r/4)*8 + 4g + r%4 of token l32; tile
+    // [128 tokens][8 chunks of 8 columns], chunk c of row r stored at c ^ (r & 7)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = i * 32 + l32, chunk = j * 4 + q;
+          u32x2 o;
+          o[0] = ET::pack2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+          o[1] = ET::pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          *reinterpret_cast<u32x2*>(stile + row * 64 + ((chunk ^ (row & 7)) * 8) + 4 * g) = o;
+        }
+    // each lane then writes 8 columns (16 bytes) of one token: 8 tokens x
+    // 128 contiguous bytes per store instruction
+    const int tl0 = lane >> 3, ch = lane & 7;
+    const int tok0 = tw + tl0;
+    int b = tok0 / a.T;
+    int t = tok0 - b * a.T;
+#pragma unroll
+    for (int rep = 0; rep < 16; ++rep) {
+      const int tl = tl0 + 8 * rep;
+      if (tw + tl < M) {
+        const size_t rowi = ((size_t)b * a.H + h) * a.Tcap + a.t_off + t;
+        uint16_t* dst = (VPART ? a.v + rowi * a.Dv : a.k + rowi * a.k_ld) + cw + ch * 8;
+        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(stile + tl * 64 + ((ch ^ (tl & 7)) * 8));
+      }
+      t += 8;
+      while (t >= a.T) {
+        t -= a.T;
+        ++b;
+      }
+    }
+  } else {
+    // C tiles: lane holds tokens (r/4)*8 + 4g + r%4 of column l32; tile
+    // [64 value columns][16 chunks of 8 tokens], chunk c of row r stored at
+    // c ^ (r & 15)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = j * 32 + l32, chunk = i * 4 + q;
+          u32x2 o;
+          o[0] = ET::pack2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+          o[1] = ET::pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          *reinterpret_cast<u32x2*>(stile + row * 128 + ((chunk ^ (row & 15)) * 8) + 4 * g) = o;
+        }
+    // each lane then writes 8 tokens (16 bytes) of one V^T row: 4 rows x
+    // 256 contiguous bytes per store instruction, when 8-token groups never
+    // straddle a sequence and stay 16-byte aligned (T and t_off multiples of
+    // 8); element stores otherwise (kept as compact loops: this path is rare
+    // and must not bloat the code)
+    const int tc = lane & 15;
+    const bool fast = (a.T % 8) == 0 && (a.t_off % 8) == 0;
+    const int tok = tw + tc * 8;
+    const int b = tok / a.T;
+    const int col = a.t_off + (tok - b * a.T);
+#pragma unroll 4
+    for (int rep = 0; rep < 16; ++rep) {
+      const int dl = (lane >> 4) + 4 * rep;
+      const int dv = cw + dl;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(stile + dl * 128 + ((tc ^ (dl & 15)) * 8));
+      if (fast) {
+        if (tok < M) {  // M is a multiple of 8 here: the whole group is in range
+          uint16_t* row = a.v + (((size_t)b * a.H + h) * a.Dv + dv) * a.v_ld;
+          *reinterpret_cast<u32x4*>(row + col) = x;
+          if (col + 7 == a.Tcap - 1) {
+#pragma unroll 1
+            for (int z = a.Tcap; z < a.v_ld; ++z) row[z] = 0;
+          }
+        }
+      } else {
+#pragma unroll 1
+        for (int e = 0; e < 8; ++e)
+          if (tok + e < M)
+            store_vt1<ET>(a, tok + e, h * (a.Dn + a.Dv) + a.Dn + dv,
+                          ET::dec((uint16_t)(x[e >> 1] >> (16 * (e & 1)))));
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------- small kernel
+namespace {
+constexpr int XS_N = 128;      // W rows (output columns) per workgroup
+constexpr int XS_M = 128;      // tokens per workgroup
+constexpr int XS_K = 32;       // reduction depth per LDS stage
+constexpr int XS_LD = XS_K + 8;  // LDS row stride (16-bit elements), 16-byte pad
 }  // namespace
 
 template <class ET>
-__global__ void __launch_bounds__(256, 2) kv_expand_kernel(ExpandArgs a, int M, int N) {
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][TN * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sAh[2][TM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sAl[2][TM * LDK];
+__global__ void __launch_bounds__(256, 2) expand_small_kernel(ExpandArgs a, int M, int N) {
+  __shared__ __attribute__((aligned(16))) uint16_t sW[2][XS_N * XS_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][XS_M * XS_LD];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
-  const int n0 = blockIdx.x * TN;
-  const int m0 = blockIdx.y * TM;
+  const int n0 = blockIdx.x * XS_N;
+  const int m0 = blockIdx.y * XS_M;
   const int R = a.R;
-  const int nstage = (R + BK - 1) / BK;
+  const int nstage = (R + XS_K - 1) / XS_K;
 
-  // W loader: chunk id = tid + 256*j (j < 2): row = id >> 2, 8 bf16 at kc*8
-  // latent loader: chunk id = tid + 256*j (j < 4): row = id >> 3, 4 fp32 at kc*4
-  u32x4 rw[2];
-  f32x4 ra[4];
+  // loaders: chunk id = tid + 256*j (j < 2): row = id >> 2, 8 elements at kc*8
+  u32x4 rw[2], ra[2];
   auto gload = [&](int s) {
-    const int k0 = s * BK;
+    const int k0 = s * XS_K;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int id = tid + 256 * j;
       const int row = id >> 2, kc = id & 3;
       const int k = k0 + kc * 8;
-      const int n = n0 + row;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      rw[j] = (n < N && k < R) ? *reinterpret_cast<const u32x4*>(a.W + (size_t)n * R + k) : z;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int id = tid + 256 * j;
-      const int row = id >> 3, kc = id & 7;
-      const int k = k0 + kc * 4;
-      const int m = m0 + row;
-      f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      // R is a multiple of 8, so a 4-wide chunk is either all inside or all outside
-      ra[j] = (m < M && k < R) ? *reinterpret_cast<const f32x4*>(a.c + (size_t)m * R + k) : z;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      // R is a multiple of 8, so an 8-wide chunk is either all inside or all outside
+      rw[j] = (n0 + row < N && k < R) ? *reinterpret_cast<const u32x4*>(a.W + (size_t)(n0 + row) * R + k) : z;
+      ra[j] = (m0 + row < M && k < R) ? *reinterpret_cast<const u32x4*>(a.c + (size_t)(m0 + row) * R + k) : z;
     }
   };
   auto lstore = [&](int buf) {
@@ -80,22 +390,8 @@ __global__ void __launch_bounds__(256, 2) kv_expand_kernel(ExpandArgs a, int M, 
     for (int j = 0; j < 2; ++j) {
       const int id = tid + 256 * j;
       const int row = id >> 2, kc = id & 3;
-      *reinterpret_cast<u32x4*>(&sW[buf][row * LDK + kc * 8]) = rw[j];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int id = tid + 256 * j;
-      const int row = id >> 3, kc = id & 7;
-      u32x2 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float x0 = ra[j][2 * e], x1 = ra[j][2 * e + 1];
-        const uint16_t h0 = f2bf(x0), h1 = f2bf(x1);
-        hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        lo[e] = pack2bf(x0 - bf2f(h0), x1 - bf2f(h1));
-      }
-      *reinterpret_cast<u32x2*>(&sAh[buf][row * LDK + kc * 4]) = hi;
-      *reinterpret_cast<u32x2*>(&sAl[buf][row * LDK + kc * 4]) = lo;
+      *reinterpret_cast<u32x4*>(&sW[buf][row * XS_LD + kc * 8]) = bf16x8_to_f16x8(rw[j]);
+      *reinterpret_cast<u32x4*>(&sA[buf][row * XS_LD + kc * 8]) = ra[j];
     }
   };
 
@@ -117,22 +413,17 @@ __global__ void __launch_bounds__(256, 2) kv_expand_kernel(ExpandArgs a, int M, 
     const int buf = s & 1;
     if (s + 1 < nstage) gload(s + 1);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 fw[2], fh[2], fl[2];
+    for (int kk = 0; kk < XS_K / 16; ++kk) {
+      u32x4 fw[2], fa[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        fw[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sW[buf][(wn * 64 + i * 32 + lrow) * LDK + kk * 16 + lk]));
-        const int ao = (wm * 64 + i * 32 + lrow) * LDK + kk * 16 + lk;
-        fh[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sAh[buf][ao]));
-        fl[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sAl[buf][ao]));
+        fw[i] = *reinterpret_cast<const u32x4*>(&sW[buf][(wn * 64 + i * 32 + lrow) * XS_LD + kk * 16 + lk]);
+        fa[i] = *reinterpret_cast<const u32x4*>(&sA[buf][(wm * 64 + i * 32 + lrow) * XS_LD + kk * 16 + lk]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          acc[i][j] = mfma32(fw[i], fl[j], acc[i][j]);
-          acc[i][j] = mfma32(fw[i], fh[j], acc[i][j]);
-        }
+        for (int j = 0; j < 2; ++j) acc[i][j] = mma16(fw[i], fa[j], acc[i][j]);
     }
     if (s + 1 < nstage) lstore(buf ^ 1);
     __syncthreads();
@@ -140,53 +431,54 @@ __global__ void __launch_bounds__(256, 2) kv_expand_kernel(ExpandArgs a, int M, 
 
   // epilogue: lane holds C^T rows n = base + (r/4)*8 + (lane/32)*4 + r%4 for
   // token column lane%32 of each 32x32 tile
-  const int DnDv = a.Dn + a.Dv;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int tok = m0 + wm * 64 + j * 32 + lrow;
     if (tok >= M) continue;
-    const int b = tok / a.T;
-    const int t = tok - b * a.T;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 64 + i * 32 + g * 8 + (lane >> 5) * 4;
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * 64 + i * 32 + q * 8 + (lane >> 5) * 4;
         if (n >= N) continue;
-        const int h = n / DnDv;
-        const int c = n - h * DnDv;
-        const size_t rowi = ((size_t)b * a.H + h) * a.Tcap + a.t_off + t;
-        if (c >= a.Dn && a.v_cols) {
-          // V^T: the four value columns are four rows of [Dv, v_ld]; the lane
-          // writing the cache's last column also zeroes the row padding
-          const int col = a.t_off + t;
-          uint16_t* dst = a.v + (((size_t)b * a.H + h) * a.Dv + (c - a.Dn)) * a.v_ld + col;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            dst[(size_t)e * a.v_ld] = ET::enc(acc[i][j][g * 4 + e]);
-            if (col == a.Tcap - 1)
-              for (int z = col + 1; z < a.v_ld; ++z) dst[(size_t)e * a.v_ld + (z - col)] = 0;
-          }
-          continue;
+        // a 4-column group never straddles a head or the k/v boundary (Dn and
+        // Dv are multiples of 8)
+        if (a.v_cols && col_info(a, n).is_v) {
+#pragma unroll 1
+          for (int e = 0; e < 4; ++e) store_vt1<ET>(a, tok, n + e, acc[i][j][q * 4 + e]);
+        } else {
+          store_row4<ET>(a, tok, n, acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2],
+                         acc[i][j][q * 4 + 3]);
         }
-        uint16_t* dst = (c < a.Dn) ? a.k + rowi * a.k_ld + c : a.v + rowi * a.Dv + (c - a.Dn);
-        u32x2 o;
-        o[0] = ET::pack2(acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1]);
-        o[1] = ET::pack2(acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]);
-        *reinterpret_cast<u32x2*>(dst) = o;
       }
     }
   }
 }
 
+template <class ET>
+static hipError_t launch_tile(const ExpandArgs& a, int M, hipStream_t stream) {
+  const dim3 gk((a.H * a.Dn + XT_N - 1) / XT_N, (M + XT_M - 1) / XT_M);
+  const dim3 gv((a.H * a.Dv + XT_N - 1) / XT_N, (M + XT_M - 1) / XT_M);
+  hipLaunchKernelGGL((expand_tile_kernel<ET, false, false>), gk, dim3(512), 0, stream, a, M);
+  if (a.v_cols)
+    hipLaunchKernelGGL((expand_tile_kernel<ET, true, true>), gv, dim3(512), 0, stream, a, M);
+  else
+    hipLaunchKernelGGL((expand_tile_kernel<ET, true, false>), gv, dim3(512), 0, stream, a, M);
+  return hipGetLastError();
+}
+
 hipError_t launch_kv_expand(const ExpandArgs& a, hipStream_t stream) {
   const int M = a.B * a.T;
   const int N = a.H * (a.Dn + a.Dv);
-  const dim3 grid((N + TN - 1) / TN, (M + TM - 1) / TM);
+  // the tile kernel needs 64-column groups that are all keys or all values
+  // and the latent width it is unrolled for
+  if (M >= 512 && (a.Dn % 64) == 0 && (a.Dv % 64) == 0 && a.R == XT_R)
+    return a.kv_dtype == F16::code ? launch_tile<F16>(a, M, stream) : launch_tile<BF16>(a, M, stream);
+  const dim3 grid((N + XS_N - 1) / XS_N, (M + XS_M - 1) / XS_M);
   if (a.kv_dtype == F16::code)
-    hipLaunchKernelGGL(kv_expand_kernel<F16>, grid, dim3(256), 0, stream, a, M, N);
+    hipLaunchKernelGGL(expand_small_kernel<F16>, grid, dim3(256), 0, stream, a, M, N);
   else
-    hipLaunchKernelGGL(kv_expand_kernel<BF16>, grid, dim3(256), 0, stream, a, M, N);
+    hipLaunchKernelGGL(expand_small_kernel<BF16>, grid, dim3(256), 0, stream, a, M, N);
   return hipGetLastError();
 }
 

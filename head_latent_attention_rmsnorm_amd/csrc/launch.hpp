@@ -24,11 +24,11 @@ struct RopeResolved {
 hipError_t launch_rope_table(const RopeResolved& r, int n_pos, float* cos_out, float* sin_out,
                              hipStream_t stream);
 
-hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* w, float eps, float* y, int n, int R,
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* w, float eps, uint16_t* y, int n, int R,
                           hipStream_t stream);
 
 struct ExpandArgs {
-  const float* c;     // [B*T, R] normalised latent, fp32
+  const uint16_t* c;  // [B*T, R] normalised latent, fp16
   const uint16_t* W;  // [N, R], N = H*(Dn+Dv)
   uint16_t* k;        // [B, H, Tcap, k_ld]
   uint16_t* v;        // [B, H, Tcap, Dv] (v_cols == 0) or [B, H, Dv, v_ld] (v_cols == 1)

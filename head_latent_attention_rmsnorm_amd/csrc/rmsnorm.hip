@@ -2,8 +2,10 @@
 // compressed latent; GLM-5 "Normalized key-value latent": default epsilon
 // 1e-6). One wavefront per row; 16-byte coalesced bf16 loads; fp32 sum of
 // squares reduced across the wavefront. The normalised latent is written in
-// fp32: kv_b_proj consumes it as an exact two-term bf16 split, so the
-// normalisation adds no bf16 rounding to the keys and values.
+// fp16 (one round-to-nearest-even per element): kv_b_proj multiplies it on
+// fp16 MFMA, and fp16's 11 significant bits keep its rounding at the level
+// of the fp16 keys and values themselves (bf16's 8 bits made it the largest
+// single error of the path).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -14,7 +16,7 @@ namespace mla {
 // 8*(l + 64*c) .. +8).
 template <int NCH>
 __global__ void __launch_bounds__(256) rmsnorm_vec_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-                                                          float eps, float* __restrict__ y, int n, int R) {
+                                                          float eps, uint16_t* __restrict__ y, int n, int R) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= n) return;
@@ -38,34 +40,27 @@ __global__ void __launch_bounds__(256) rmsnorm_vec_kernel(const uint16_t* __rest
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)R + eps);
   const u32x4* wr = reinterpret_cast<const u32x4*>(w);
-  f32x4* yr = reinterpret_cast<f32x4*>(y + (size_t)row * R);
+  u32x4* yr = reinterpret_cast<u32x4*>(y + (size_t)row * R);
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int ch = lane + 64 * c;
     if (ch < nch) {
       const u32x4 g = wr[ch];
-      f32x4 o0, o1;
+      u32x4 o;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float a = __uint_as_float(v[c][j] << 16) * r * __uint_as_float(g[j] << 16);
         const float b = __uint_as_float(v[c][j] & 0xffff0000u) * r * __uint_as_float(g[j] & 0xffff0000u);
-        if (j < 2) {
-          o0[2 * j] = a;
-          o0[2 * j + 1] = b;
-        } else {
-          o1[2 * j - 4] = a;
-          o1[2 * j - 3] = b;
-        }
+        o[j] = pack2h(a, b);
       }
-      yr[2 * ch] = o0;
-      yr[2 * ch + 1] = o1;
+      yr[ch] = o;
     }
   }
 }
 
 // Any width: two passes over the row with scalar loads.
 __global__ void __launch_bounds__(256) rmsnorm_any_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-                                                          float eps, float* __restrict__ y, int n, int R) {
+                                                          float eps, uint16_t* __restrict__ y, int n, int R) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= n) return;
@@ -77,11 +72,11 @@ __global__ void __launch_bounds__(256) rmsnorm_any_kernel(const uint16_t* __rest
   }
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)R + eps);
-  float* yr = y + (size_t)row * R;
-  for (int i = lane; i < R; i += 64) yr[i] = bf2f(xr[i]) * r * bf2f(w[i]);
+  uint16_t* yr = y + (size_t)row * R;
+  for (int i = lane; i < R; i += 64) yr[i] = f2h(bf2f(xr[i]) * r * bf2f(w[i]));
 }
 
-hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* w, float eps, float* y, int n, int R,
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* w, float eps, uint16_t* y, int n, int R,
                           hipStream_t stream) {
   const dim3 grid((n + 3) / 4), block(256);
   const bool aligned = ((((uintptr_t)x) | ((uintptr_t)w) | ((uintptr_t)y)) & 15) == 0;

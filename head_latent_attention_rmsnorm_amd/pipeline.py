@@ -44,7 +44,7 @@ def alloc_prefill(B, T, H, R, Dn, Dr, Dv, device="cuda", kv_dtype=torch.float16)
     size and MFMA rate as bf16 on gfx950, three more significant bits). The
     values are kept transposed (V^T), the layout the attention reads."""
     return PrefillBuffers(
-        c_norm=torch.empty((B, T, R), dtype=torch.float32, device=device),
+        c_norm=torch.empty((B, T, R), dtype=torch.float16, device=device),
         k_nope=torch.empty((B, H, T, Dn), dtype=kv_dtype, device=device),
         v=torch.empty((B, H, Dv, api.round8(T)), dtype=kv_dtype, device=device),
         out=torch.empty((B, H, T, Dv), dtype=torch.bfloat16, device=device),

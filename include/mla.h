@@ -138,28 +138,31 @@ mla_status mla_rope_table_build(const mla_rope_params* p, int32_t n_pos, float* 
 mla_status mla_softmax_scale(const mla_rope_params* p, int32_t qk_head_dim, double* scale_out);
 
 /* Latent RMSNorm [eq; GLM-kv: kv_a_layernorm built without epsilon, i.e.
- * 1e-6]: y[r, :] = w * x[r, :] / sqrt(mean(x[r, :]^2) + eps), computed and
- * written in fp32. The normalised latent is kept in fp32 because kv_b_proj
- * consumes it exactly (see mla_kv_expand): rounding it to bf16 would be the
- * largest single error of the whole path.
- * Args: x device bf16 [n, R]; w device bf16 [R]; eps >= 0; y device fp32
+ * 1e-6]: y[r, :] = w * x[r, :] / sqrt(mean(x[r, :]^2) + eps), computed in
+ * fp32 and written in fp16 (one round-to-nearest-even per element; values
+ * must stay below 65504 in magnitude). fp16 rather than the model dtype bf16:
+ * kv_b_proj multiplies the latent on fp16 MFMA, and fp16's 11 significant
+ * bits keep its rounding at the level of the fp16 keys and values, where
+ * bf16's 8 would be the largest single error of the whole path.
+ * Args: x device bf16 [n, R]; w device bf16 [R]; eps >= 0; y device fp16
  *   [n, R]; n >= 0 rows (0 is a no-op); 1 <= R <= 8192.
  * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_HIP. */
-mla_status mla_latent_rmsnorm(const mla_bf16* x, const mla_bf16* w, float eps, float* y, int32_t n,
+mla_status mla_latent_rmsnorm(const mla_bf16* x, const mla_bf16* w, float eps, uint16_t* y, int32_t n,
                               int32_t R, hipStream_t stream);
 
 /* kv_b_proj up-projection and head split [eq; GLM-kv expand_kv]:
  *   kv[b, t, :] = c_norm[b, t, :] . W^T, viewed [H, Dn+Dv]; for each head h
  *   k[b, h, t_off + t, 0:Dn]  = kv[b, t, h*(Dn+Dv) + 0 .. Dn)
  *   v[b, h, t_off + t, 0:Dv]  = kv[b, t, h*(Dn+Dv) + Dn .. Dn+Dv)
- * bf16 MFMA with fp32 accumulation, one RNE rounding per output to kv_dtype.
- * The fp32 latent enters the MFMA as two bf16 terms, hi = bf16(c) and
- * lo = bf16(c - hi), which carry it to 16 significant bits.
+ * fp16 MFMA with fp32 accumulation, one RNE rounding per output to kv_dtype.
+ * W (bf16) is widened to fp16, exact for every bf16 value of magnitude at
+ * least 2^-24 (smaller ones round to fp16 subnormals or zero, far below the
+ * fp32 resolution of the sums).
  * Append mode (k_pe != NULL), the expanded-cache update of a decode step
  * [K2-query]: additionally the shared rotary key of token (b, t) is rotated
  * at position pos[b*T + t] (or t_off + t when pos is NULL) with the table
  * and written to k[b, h, t_off + t, Dn : Dn+Dr] for every head h.
- * Args: c_norm device fp32 [B, T, R] (from mla_latent_rmsnorm); W device
+ * Args: c_norm device fp16 [B, T, R] (from mla_latent_rmsnorm); W device
  *   bf16 [H*(Dn+Dv), R]
  *   (nn.Linear weight layout); k device [B, H, Tcap, k_ld] and v device
  *   [B, H, Tcap, Dv] (v_layout MLA_V_ROWS, v_ld ignored) or V^T
@@ -174,7 +177,7 @@ mla_status mla_latent_rmsnorm(const mla_bf16* x, const mla_bf16* w, float eps, f
  *   B*T == 0 is a no-op.
  * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_ROPE_TYPE (pairing),
  *   MLA_ERR_UNSUPPORTED (kv_dtype), MLA_ERR_HIP. */
-mla_status mla_kv_expand(const float* c_norm, const mla_bf16* W, int32_t B, int32_t T,
+mla_status mla_kv_expand(const uint16_t* c_norm, const mla_bf16* W, int32_t B, int32_t T,
                          int32_t R, int32_t H, int32_t Dn, int32_t Dv, uint16_t* k, int32_t k_ld,
                          uint16_t* v, int32_t v_layout, int32_t v_ld, int32_t Tcap, int32_t t_off,
                          int32_t kv_dtype,
