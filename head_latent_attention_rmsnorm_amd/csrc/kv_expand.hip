@@ -26,9 +26,12 @@
 //    columns of one token: one 8-byte store into a k_nope / v row). Swapping
 //    the two MFMA operands is all it takes: an A and a B fragment have the
 //    same lane layout.
+//  - expand_skinny_kernel: at most 32 tokens (the decode append): one wave per
+//    32 columns, operands loaded from global memory straight into registers.
 //  - expand_small_kernel: 128 columns x 128 tokens, 4 waves, everything staged
-//    through registers; any shape (used for few tokens, e.g. the decode
-//    append, and head widths that are not multiples of 64).
+//    through registers; any other shape (a few hundred tokens, head widths
+//    that are not multiples of 64, latent widths that are not multiples of
+//    128).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -455,6 +458,55 @@ __global__ void __launch_bounds__(256, 2) expand_small_kernel(ExpandArgs a, int 
   }
 }
 
+// -------------------------------------------------------------- skinny kernel
+// Few tokens (M <= 32, the decode append): the work is reading W once. One
+// wave per 32 output columns computes C^T = W c^T for all (up to 32) tokens;
+// every MFMA operand is one 16-byte run of a W or latent row, loaded straight
+// from global memory into registers (no LDS), W widened to fp16 on the way.
+template <class ET>
+__global__ void __launch_bounds__(64) expand_skinny_kernel(ExpandArgs a, int M, int N) {
+  const int lane = threadIdx.x;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int n0 = blockIdx.x * 32;
+  const int R = a.R;
+  // A operand: W row n0 + l32 (rows past N read row 0: their outputs are not
+  // stored); B operand: latent row l32 (tokens past M read as zeros)
+  const int wn = n0 + l32 < N ? n0 + l32 : 0;
+  const uint16_t* wr = a.W + (size_t)wn * R + 8 * g;
+  const bool tok_ok = l32 < M;
+  const uint16_t* cr = a.c + (size_t)(tok_ok ? l32 : 0) * R + 8 * g;
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  // 8 MFMA steps (128 reduction elements) per round; R is a multiple of 128
+  for (int k0 = 0; k0 < R; k0 += 128) {
+    u32x4 wf[8], cf[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      wf[ks] = *reinterpret_cast<const u32x4*>(wr + k0 + 16 * ks);
+      cf[ks] = tok_ok ? *reinterpret_cast<const u32x4*>(cr + k0 + 16 * ks) : z;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) acc = mma16(bf16x8_to_f16x8(wf[ks]), cf[ks], acc);
+  }
+  // lane holds columns n0 + (r/4)*8 + 4g + r%4 of token l32
+  if (!tok_ok) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int n = n0 + q * 8 + 4 * g;
+    if (n >= N) continue;
+    // a 4-column group never straddles a head or the k/v boundary (Dn and Dv
+    // are multiples of 8)
+    if (a.v_cols && col_info(a, n).is_v) {
+#pragma unroll 1
+      for (int e = 0; e < 4; ++e) store_vt1<ET>(a, l32, n + e, acc[q * 4 + e]);
+    } else {
+      store_row4<ET>(a, l32, n, acc[q * 4 + 0], acc[q * 4 + 1], acc[q * 4 + 2], acc[q * 4 + 3]);
+    }
+  }
+}
+
 template <class ET>
 static hipError_t launch_tile(const ExpandArgs& a, int M, hipStream_t stream) {
   const dim3 gk((a.H * a.Dn + XT_N - 1) / XT_N, (M + XT_M - 1) / XT_M);
@@ -474,6 +526,14 @@ hipError_t launch_kv_expand(const ExpandArgs& a, hipStream_t stream) {
   // and the latent width it is unrolled for
   if (M >= 512 && (a.Dn % 64) == 0 && (a.Dv % 64) == 0 && a.R == XT_R)
     return a.kv_dtype == F16::code ? launch_tile<F16>(a, M, stream) : launch_tile<BF16>(a, M, stream);
+  if (M <= 32 && (a.R % 128) == 0) {
+    const dim3 grid((N + 31) / 32);
+    if (a.kv_dtype == F16::code)
+      hipLaunchKernelGGL(expand_skinny_kernel<F16>, grid, dim3(64), 0, stream, a, M, N);
+    else
+      hipLaunchKernelGGL(expand_skinny_kernel<BF16>, grid, dim3(64), 0, stream, a, M, N);
+    return hipGetLastError();
+  }
   const dim3 grid((N + XS_N - 1) / XS_N, (M + XS_M - 1) / XS_M);
   if (a.kv_dtype == F16::code)
     hipLaunchKernelGGL(expand_small_kernel<F16>, grid, dim3(256), 0, stream, a, M, N);

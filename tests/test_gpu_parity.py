@@ -84,6 +84,8 @@ EXPAND_SHAPES = [
     dict(B=2, T=150, H=3, R=64, Dn=32, Dv=32),        # small kernel: ragged tokens and columns
     dict(B=1, T=513, H=4, R=512, Dn=192, Dv=256),     # GLM-5 head widths, tile kernel
     dict(B=3, T=1, H=5, R=104, Dn=8, Dv=24),          # reduction not a multiple of the stage
+    dict(B=4, T=5, H=3, R=512, Dn=128, Dv=128),       # skinny kernel (few tokens, decode-append sized)
+    dict(B=1, T=30, H=5, R=256, Dn=32, Dv=32),        # skinny kernel, ragged columns
 ]
 
 
