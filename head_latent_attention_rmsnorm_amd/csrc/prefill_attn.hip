@@ -130,38 +130,41 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
       u32x4 raw = {0u, 0u, 0u, 0u};
       if (valid) raw = *reinterpret_cast<const u32x4*>(qrow + d0);
       if (d0 >= DN) {
-        // rotary part: rotate in fp32, round once to the operand type
+        // rotary part: rotate in fp32, round once to the operand type. The
+        // chunk's 8 elements use 8 consecutive pairs (half pairing; the
+        // partners are the matching chunk of the other half) or 4 (interleaved:
+        // the partner is the other half of each word), so cos and sin arrive
+        // as 16-byte loads of the position's table row.
         const int re0 = d0 - DN;  // rotary index of the chunk's first element
-        u32x4 partner = raw;
-        if (!a.pairing) {
-          const int pre0 = re0 < DR / 2 ? re0 + DR / 2 : re0 - DR / 2;
-          if (valid) partner = *reinterpret_cast<const u32x4*>(qrow + DN + pre0);
-        }
+        const float* crow = a.cos + (size_t)p * (DR / 2);
+        const float* srow = a.sin + (size_t)p * (DR / 2);
         u32x4 outv;
+        if (!a.pairing) {
+          const bool first = re0 < DR / 2;
+          const int pi0 = first ? re0 : re0 - DR / 2;
+          u32x4 partner = {0u, 0u, 0u, 0u};
+          if (valid) partner = *reinterpret_cast<const u32x4*>(qrow + DN + (first ? re0 + DR / 2 : re0 - DR / 2));
+          const f32x4 c0 = *reinterpret_cast<const f32x4*>(crow + pi0);
+          const f32x4 c1 = *reinterpret_cast<const f32x4*>(crow + pi0 + 4);
+          const f32x4 s0 = *reinterpret_cast<const f32x4*>(srow + pi0);
+          const f32x4 s1 = *reinterpret_cast<const f32x4*>(srow + pi0 + 4);
+          const float sgn = first ? -1.0f : 1.0f;  // (x cos - x' sin) for the first half, (x cos + x' sin) after
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          float y[2];
-#pragma unroll
-          for (int hl = 0; hl < 2; ++hl) {
-            const int re = re0 + 2 * e2 + hl;
-            const float x = hl ? __uint_as_float(raw[e2] & 0xffff0000u) : __uint_as_float(raw[e2] << 16);
-            float xp;
-            int pi;
-            bool first;
-            if (a.pairing) {  // interleaved: the partner is the other half of the word
-              xp = hl ? __uint_as_float(raw[e2] << 16) : __uint_as_float(raw[e2] & 0xffff0000u);
-              pi = re >> 1;
-              first = (re & 1) == 0;
-            } else {
-              xp = hl ? __uint_as_float(partner[e2] & 0xffff0000u) : __uint_as_float(partner[e2] << 16);
-              pi = re < DR / 2 ? re : re - DR / 2;
-              first = re < DR / 2;
-            }
-            const float cs = a.cos[(size_t)p * (DR / 2) + pi];
-            const float sn = a.sin[(size_t)p * (DR / 2) + pi];
-            y[hl] = (first ? (x * cs - xp * sn) : (x * cs + xp * sn)) * qmul;
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const float cs0 = e2 < 2 ? c0[2 * e2] : c1[2 * e2 - 4], cs1 = e2 < 2 ? c0[2 * e2 + 1] : c1[2 * e2 - 3];
+            const float sn0 = e2 < 2 ? s0[2 * e2] : s1[2 * e2 - 4], sn1 = e2 < 2 ? s0[2 * e2 + 1] : s1[2 * e2 - 3];
+            const float x0 = __uint_as_float(raw[e2] << 16), x1 = __uint_as_float(raw[e2] & 0xffff0000u);
+            const float p0 = __uint_as_float(partner[e2] << 16), p1 = __uint_as_float(partner[e2] & 0xffff0000u);
+            outv[e2] = ET::pack2((x0 * cs0 + sgn * (p0 * sn0)) * qmul, (x1 * cs1 + sgn * (p1 * sn1)) * qmul);
           }
-          outv[e2] = ET::pack2(y[0], y[1]);
+        } else {
+          const f32x4 cs = *reinterpret_cast<const f32x4*>(crow + (re0 >> 1));
+          const f32x4 sn = *reinterpret_cast<const f32x4*>(srow + (re0 >> 1));
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const float x0 = __uint_as_float(raw[e2] << 16), x1 = __uint_as_float(raw[e2] & 0xffff0000u);
+            outv[e2] = ET::pack2((x0 * cs[e2] - x1 * sn[e2]) * qmul, (x1 * cs[e2] + x0 * sn[e2]) * qmul);
+          }
         }
         raw = outv;
       } else if (FOLD || ET::code != BF16::code) {
@@ -181,47 +184,52 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
   // the lane's accumulator registers 8*(r>>3) .. hold consecutive keys
   const int krow = 16 * ((l32 >> 3) >> 1) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
 
-  // per-lane byte offsets of this wave's operand blocks, relative to the
-  // tile's first key (fixed over the key loop)
-  uint32_t voff[LPW];
+  // This wave's operand blocks: for each, the buffer descriptor of the whole
+  // (b, h) slice it comes from (chosen once here, kept in scalar registers),
+  // the lane's byte offset for the tile starting at key 0, and the bytes one
+  // key advances it. The tile offset goes into the vector offset, which the
+  // descriptor's range check covers: keys past the end of the sequence read
+  // as zeros. (Choosing descriptors per tile instead costs tens of scalar
+  // instructions per wave, and the 8 waves reach that point together right
+  // after the barrier, queueing on the CU's one scalar unit.)
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_nope + bh * T * DN, (uint32_t)T * DN * 2u);
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.k_rot + (size_t)b * T * DR, (uint32_t)T * DR * 2u);
+  const __amdgpu_buffer_rsrc_t rv =
+      make_rsrc(a.v + bh * (size_t)DV * a.v_ld, (uint32_t)DV * (uint32_t)a.v_ld * 2u);
+  __amdgpu_buffer_rsrc_t rs[LPW];
+  uint32_t voff[LPW], vstep[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int bi = wave + NW * i;
-    uint32_t o = 0;
+    rs[i] = rv;
+    voff[i] = 0;
+    vstep[i] = 0;
     if (bi < KBLK) {
       const int j = bi / QC, c = bi % QC;
       const int row = 32 * j + krow;
-      o = (16 * c < DN) ? (uint32_t)(row * DN + 16 * c + 8 * g) * 2u
-                        : (uint32_t)(row * DR + (16 * c - DN) + 8 * g) * 2u;
+      if (16 * c < DN) {
+        rs[i] = rk;
+        voff[i] = (uint32_t)(row * DN + 16 * c + 8 * g) * 2u;
+        vstep[i] = DN * 2u;
+      } else {
+        rs[i] = rr;
+        voff[i] = (uint32_t)(row * DR + (16 * c - DN) + 8 * g) * 2u;
+        vstep[i] = DR * 2u;
+      }
     } else if (bi < NBLK) {
       const int vb = bi - KBLK, d = vb / NPV, m = vb % NPV;
-      o = (uint32_t)((32 * d + l32) * a.v_ld + 16 * m + 8 * g) * 2u;
+      voff[i] = (uint32_t)((32 * d + l32) * a.v_ld + 16 * m + 8 * g) * 2u;
+      vstep[i] = 2u;
     }
-    voff[i] = o;
   }
-  const uint16_t* kn_base = a.k_nope + bh * T * DN;
-  const uint16_t* kr_base = a.k_rot + (size_t)b * T * DR;
-  const uint16_t* vt_base = a.v + bh * (size_t)DV * a.v_ld;
-  const uint32_t vt_elems = (uint32_t)DV * (uint32_t)a.v_ld;
 
   // queue the LDS-direct loads of key tile kt into buffer buf
   auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
-    const int key0 = kt * BN;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kn_base + (size_t)key0 * DN, (uint32_t)(T - key0) * DN * 2u);
-    const __amdgpu_buffer_rsrc_t rr = make_rsrc(kr_base + (size_t)key0 * DR, (uint32_t)(T - key0) * DR * 2u);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vt_base + key0, (vt_elems - (uint32_t)key0) * 2u);
+    const uint32_t key0 = (uint32_t)(kt * BN);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int bi = wave + NW * i;
-      if (bi < NBLK) {
-        void* dst = &smem[buf][bi * 64];
-        if (bi >= KBLK)
-          load_lds16(rv, dst, voff[i]);
-        else if (16 * (bi % QC) < DN)
-          load_lds16(rk, dst, voff[i]);
-        else
-          load_lds16(rr, dst, voff[i]);
-      }
+      if (bi < NBLK) load_lds16(rs[i], &smem[buf][bi * 64], voff[i] + key0 * vstep[i]);
     }
   };
 
