@@ -18,14 +18,20 @@
 //  - values arrive transposed (V^T, keys contiguous per value column), so
 //    both products read their A operands as 8 consecutive 16-bit elements;
 //  - K and V^T tiles move global -> LDS with 16-byte buffer loads that write
-//    LDS directly (no registers, no LDS store instructions). The LDS image is
-//    fragment-major: one 1 KB block per (32-key sub-tile, 16-deep k-step) or
-//    (32-value tile, 16-key step) holds the 64 lanes' MFMA operands in lane
-//    order, so every operand read is one conflict-free 16-byte LDS read. The
-//    gather into that order happens in the loads' per-lane addresses, which
-//    stay fixed over the key loop (the tile offset moves the buffer
-//    descriptor's base); the descriptor's range check returns zeros past the
-//    end of the sequence. Tiles are double-buffered, one barrier per tile;
+//    LDS directly (no registers, no LDS store instructions): lane i of a load
+//    writes bytes 16i..16i+15 of a 1 KB block. A group of SW such blocks
+//    holds SW consecutive 16-deep k-steps of the 32 operand rows one MFMA
+//    reads (32 keys of K, 32 value columns of V^T): each block carries
+//    32/SW whole rows of the group, 32*SW contiguous bytes each, so one load
+//    instruction reads 8 full 128-byte lines from memory when SW is 4. The
+//    16-byte chunks of a row are stored XOR-permuted by a function of the
+//    row, which spreads the 16 lanes of one LDS read cycle over all 64
+//    banks: every operand read is one conflict-free 16-byte LDS read, at a
+//    per-lane address that only flips bits for the next k-step. The gather
+//    into that order happens in the loads' per-lane addresses, which stay
+//    fixed over the key loop; the descriptor's range check returns zeros
+//    past the end of the sequence. Tiles are double-buffered, one barrier
+//    per tile;
 //  - the K rows of a 32-key sub-tile are gathered in a permuted order, chosen
 //    so that the 8 scores a lane holds for one 16-key step of P V are 8
 //    consecutive keys: P goes from the S accumulator to a 16-bit B operand of
@@ -72,6 +78,30 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, 0, 0, 0);
 }
+
+// Operand groups of SW 1 KB blocks (SW = 1, 2 or 4 k-steps of 16 elements
+// for 32 operand rows). Row r (0..31) lives in block r / (32/SW) of the
+// group at byte (r % (32/SW)) * 32*SW; its 16-byte chunk x (0..2SW-1) sits
+// at chunk position x ^ swz(r). With 16 lanes per LDS cycle (rows r..r+15
+// of one k-step, same chunk), the pairs (row position mod 256 bytes, chunk
+// position) are all distinct, so the 16 reads hit 16 different 4-bank groups.
+template <int SW>
+__device__ __forceinline__ int frag_swz(int r) {
+  return (r >> (SW == 4 ? 1 : SW == 2 ? 2 : 3)) & (2 * SW - 1);
+}
+// Byte offset in the group of the chunk that lane (row r, half g) reads for
+// k-step 0; k-step c is at this offset XOR 32c.
+template <int SW>
+__device__ __forceinline__ int frag_read0(int r, int g) {
+  constexpr int RL = 32 / SW;
+  return (r / RL) * 1024 + (r % RL) * (32 * SW) + ((frag_swz<SW>(r) ^ g) << 4);
+}
+// Row r and chunk x that load lane i writes into block rb of a group.
+template <int SW>
+__device__ __forceinline__ void frag_slot(int rb, int i, int& r, int& x) {
+  r = rb * (32 / SW) + i / (2 * SW);
+  x = (i % (2 * SW)) ^ frag_swz<SW>(r);
+}
 }  // namespace
 
 template <class ET, int DQK, int DR, int DV, int BN, int NW, int MINW>
@@ -86,6 +116,10 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
   constexpr int LPW = (NBLK + NW - 1) / NW;  // LDS-direct loads per wave per tile
   constexpr int BMW = NW * 32;          // query rows per workgroup
   constexpr bool FOLD = ET::code == F16::code;  // scores leave the MFMA as exp2 arguments
+  // k-steps per operand group (see frag_read0): K groups must not straddle
+  // the nope|rope boundary
+  constexpr int SWK = (DN % 64 == 0 && DR % 64 == 0) ? 4 : (DN % 32 == 0 && DR % 32 == 0) ? 2 : 1;
+  constexpr int SWV = (NPV % 4 == 0) ? 4 : (NPV % 2 == 0) ? 2 : 1;
   static_assert(DN % 16 == 0 && DR % 16 == 0 && DV % 32 == 0 && BN % 32 == 0, "tile shape");
 
   __shared__ __attribute__((aligned(16))) u32x4 smem[2][NBLK * 64];
@@ -180,9 +214,10 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
   const int kend = min(T, (qt + 1) * BMW);  // keys [0, kend) are visible to some row
   const int nkt = (kend + BN - 1) / BN;
 
-  // K row gathered by this lane for the S^T MFMA: the permutation that makes
-  // the lane's accumulator registers 8*(r>>3) .. hold consecutive keys
-  const int krow = 16 * ((l32 >> 3) >> 1) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
+  // Key (within a 32-key sub-tile) of operand row r of the S^T MFMA: the
+  // permutation that makes a lane's accumulator registers 8*(i>>3) .. hold
+  // consecutive keys
+  auto krow = [](int r) { return 16 * ((r >> 3) >> 1) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3); };
 
   // This wave's operand blocks: for each, the buffer descriptor of the whole
   // (b, h) slice it comes from (chosen once here, kept in scalar registers),
@@ -205,20 +240,25 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
     voff[i] = 0;
     vstep[i] = 0;
     if (bi < KBLK) {
-      const int j = bi / QC, c = bi % QC;
-      const int row = 32 * j + krow;
-      if (16 * c < DN) {
+      const int j = bi / QC, cq = bi % QC;
+      int r, x;
+      frag_slot<SWK>(cq % SWK, lane, r, x);
+      const int row = 32 * j + krow(r);
+      const int col = (cq / SWK) * (16 * SWK) + 8 * x;
+      if (col < DN) {
         rs[i] = rk;
-        voff[i] = (uint32_t)(row * DN + 16 * c + 8 * g) * 2u;
+        voff[i] = (uint32_t)(row * DN + col) * 2u;
         vstep[i] = DN * 2u;
       } else {
         rs[i] = rr;
-        voff[i] = (uint32_t)(row * DR + (16 * c - DN) + 8 * g) * 2u;
+        voff[i] = (uint32_t)(row * DR + (col - DN)) * 2u;
         vstep[i] = DR * 2u;
       }
     } else if (bi < NBLK) {
-      const int vb = bi - KBLK, d = vb / NPV, m = vb % NPV;
-      voff[i] = (uint32_t)((32 * d + l32) * a.v_ld + 16 * m + 8 * g) * 2u;
+      const int vb = bi - KBLK, d = vb / NPV, s = vb % NPV;
+      int r, x;
+      frag_slot<SWV>(s % SWV, lane, r, x);
+      voff[i] = (uint32_t)((32 * d + r) * a.v_ld + (s / SWV) * (16 * SWV) + 8 * x) * 2u;
       vstep[i] = 2u;
     }
   }
@@ -251,15 +291,28 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
   // MFMAs of sub-tile j+1 are issued before the softmax of sub-tile j, and
   // the PV MFMAs of sub-tile j before the softmax of j+1, so the exp and
   // conversion work of one sub-tile can run under the MFMAs of another.
+  // this lane's operand read offsets for each k-step position in a group
+  int rdk[SWK], rdv[SWV];
+#pragma unroll
+  for (int c = 0; c < SWK; ++c) rdk[c] = frag_read0<SWK>(l32, g) ^ (32 * c);
+#pragma unroll
+  for (int c = 0; c < SWV; ++c) rdv[c] = frag_read0<SWV>(l32, g) ^ (32 * c);
+
   auto tile = [&](int cur, int key0) __attribute__((always_inline)) {
-    const u32x4* blk = &smem[cur][lane];
+    const char* sb = reinterpret_cast<const char*>(&smem[cur][0]);
+    auto kfrag = [&](int j, int c) __attribute__((always_inline)) {
+      return *reinterpret_cast<const u32x4*>(sb + (j * QC + (c / SWK) * SWK) * 1024 + rdk[c % SWK]);
+    };
+    auto vfrag = [&](int d, int s) __attribute__((always_inline)) {
+      return *reinterpret_cast<const u32x4*>(sb + (KBLK + d * NPV + (s / SWV) * SWV) * 1024 + rdv[s % SWV]);
+    };
     const bool diag = key0 + BN - 1 > qlo;  // the tile crosses the wave's diagonal
     f32x16 sacc[NSUB];
     u32x4 pf[NPV];
     auto s_chain = [&](int j) __attribute__((always_inline)) {
       u32x4 kf[QC];
 #pragma unroll
-      for (int c = 0; c < QC; ++c) kf[c] = blk[(j * QC + c) * 64];
+      for (int c = 0; c < QC; ++c) kf[c] = kfrag(j, c);
       __builtin_amdgcn_sched_barrier(0);
       sacc[j] = ET::mma(kf[0], qf[0], negm);
 #pragma unroll
@@ -343,7 +396,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
       for (int d = 0; d < NO; ++d)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm)
-          oacc[d] = ET::mma(blk[(KBLK + d * NPV + 2 * j + mm) * 64], pf[2 * j + mm], oacc[d]);
+          oacc[d] = ET::mma(vfrag(d, 2 * j + mm), pf[2 * j + mm], oacc[d]);
     }
   };
 
