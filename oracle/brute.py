@@ -162,3 +162,30 @@ def decode(w, inp):
             ob.append([_attend(qrow, [keys[s] for s in visible], [vals[s] for s in visible], scale)])
         out.append(ob)
     return out
+
+
+def decode_latent(w, inp, q_pos=None):
+    """O[b][h][0][j] for a tiny decode workload with a compressed-latent
+    cache, by scalar loops: the new token's row q_pos[b] of the cache takes
+    its normalised latent and rotated rotary key, every row 0..q_pos[b] is
+    expanded by kv_b_proj, and the query attends to those rows."""
+    q, lat, kpe = _flat(inp["q"]), _flat(inp["latent"]), _flat(inp["k_pe"])
+    gain, Wl = _flat(inp["gain"]), _flat(inp["W"])
+    cache = _flat(inp["latent_cache"])
+    freqs = inv_freq(w.rope, w.Dr)
+    m = mscale_ratio(w.rope)
+    scale = scale_of(w.rope, w.Dqk)
+    out = []
+    for b in range(w.B):
+        p = w.q_pos if q_pos is None else int(q_pos[b])
+        rows = [list(cache[b][s]) for s in range(p + 1)]
+        rows[p] = _norm_row(lat[b][0], gain, w.eps) + rot(kpe[b][0], p, freqs, m, w.pairing)
+        expanded = [_expand_token(r[:w.R], Wl, w.H, w.Dn, w.Dv) for r in rows]
+        ob = []
+        for h in range(w.H):
+            keys = [expanded[s][0][h] + rows[s][w.R:] for s in range(p + 1)]
+            vals = [expanded[s][1][h] for s in range(p + 1)]
+            qrow = q[b][h][0][:w.Dn] + rot(q[b][h][0][w.Dn:], p, freqs, m, w.pairing)
+            ob.append([_attend(qrow, keys, vals, scale)])
+        out.append(ob)
+    return out

@@ -22,7 +22,9 @@ each step follows:
   [GLM-kv]    GLM-5 "Normalized key-value latent", section "Key-value
               compression" (RMSNorm default epsilon 1e-6, kv_b_proj shape,
               expand_kv, shared rotary key broadcast to all heads, softmax
-              scale 1/sqrt(256) under default RoPE) and section "KV cache".
+              scale 1/sqrt(256) under default RoPE) and section "KV cache"
+              (per token the cache keeps the normalised latent and the
+              rotated rotary key, and re-expands them on every call).
 
 Readings of points the pages leave open are listed beside the functions that
 take them (RMSNorm body, rotation pairing and sign, default RoPE body).
@@ -337,4 +339,80 @@ def decode(w, inp: dict) -> np.ndarray:
     for b in range(w.B):
         for h in range(w.H):
             O[b, h] = decode_head(w, inp, parts, b, h)
+    return O
+
+
+# ---------------------------------------------------------------------------
+# Decode against a compressed-latent cache [eq], [GLM-kv]
+# ---------------------------------------------------------------------------
+
+
+def _latent_decode_setup(w, inp: dict, b_idx=None, q_pos=None):
+    """The latent cache [b, L, R+Dr] after the decode step's update, the
+    non-rotary query, the rotated rotary query and the query positions.
+
+    The cache row of a token holds its normalised latent (R values) followed
+    by its rotated shared rotary key (Dr values): what the GLM-5 page's
+    "KV cache" section keeps per token instead of expanded keys and values.
+    Rows other than the new token's are used as given. The new token of
+    sequence b sits at position q_pos[b]: its latent is normalised and its
+    rotary key rotated at that position, and both replace row q_pos[b]."""
+    bs = slice(None) if b_idx is None else np.asarray(b_idx)
+    cache = _f64(inp["latent_cache"][bs]).copy()
+    nb = cache.shape[0]
+    qp = np.full(nb, w.q_pos, dtype=np.int64) if q_pos is None else np.asarray(q_pos, dtype=np.int64)
+    c_new = rmsnorm(_f64(inp["latent"][bs]), _f64(inp["gain"]), w.eps)  # [b,1,R]
+    cos, sin = rope_table(w.rope, w.Dr, int(qp.max()) + 1)
+    q = _f64(inp["q"][bs])
+    q_pe = np.empty_like(q[..., w.Dn:])
+    kpe = _f64(inp["k_pe"][bs])
+    for i in range(nb):
+        p = int(qp[i])
+        q_pe[i] = rotate(q[i, :, :, w.Dn:], cos[p], sin[p], w.pairing)
+        cache[i, p, :w.R] = c_new[i, 0]
+        cache[i, p, w.R:] = rotate(kpe[i, 0], cos[p], sin[p], w.pairing)
+    return cache, q[..., :w.Dn], q_pe, qp
+
+
+def decode_latent(w, inp: dict, b_idx=None, q_pos=None) -> np.ndarray:
+    """Decode output O [b, H, 1, Dv] against a compressed-latent cache, by
+    the definition: every cached latent is expanded by kv_b_proj into
+    per-head non-rotary keys and values [eq], each head's key is joined with
+    the shared rotated rotary key [GLM-kv, expand_kv], and the query at
+    position q_pos[b] attends to rows 0..q_pos[b] [K2-query]."""
+    cache, q_nope, q_pe, qp = _latent_decode_setup(w, inp, b_idx, q_pos)
+    W = _f64(inp["W"])
+    scale = softmax_scale(w.rope, w.Dqk)
+    O = np.empty((cache.shape[0], w.H, 1, w.Dv), dtype=np.float64)
+    for i in range(cache.shape[0]):
+        p = int(qp[i])
+        rows = cache[i, :p + 1]
+        k_nope, v = kv_expand(rows[None, :, :w.R], W, w.H, w.Dn, w.Dv)  # [1,H,p+1,*]
+        pos = np.arange(p + 1)
+        for h in range(w.H):
+            K = np.concatenate([k_nope[0, h], rows[:, w.R:]], axis=-1)
+            Q = np.concatenate([q_nope[i, h], q_pe[i, h]], axis=-1)
+            O[i, h] = attention(Q, K, v[0, h], scale, np.array([p]), pos)
+    return O
+
+
+def decode_latent_absorbed(w, inp: dict, b_idx=None, q_pos=None) -> np.ndarray:
+    """The same output by the absorbed form [eq]: W_uk folded into the
+    non-rotary query, scores against the cached latent and rotary key, W_uv
+    applied to the probability-weighted latent. Algebraically equal to
+    `decode_latent`."""
+    cache, q_nope, q_pe, qp = _latent_decode_setup(w, inp, b_idx, q_pos)
+    W = _f64(inp["W"]).reshape(w.H, w.Dn + w.Dv, w.R)
+    W_uk, W_uv = W[:, :w.Dn, :], W[:, w.Dn:, :]
+    scale = softmax_scale(w.rope, w.Dqk)
+    O = np.empty((cache.shape[0], w.H, 1, w.Dv), dtype=np.float64)
+    for i in range(cache.shape[0]):
+        p = int(qp[i])
+        rows = cache[i, :p + 1]
+        for h in range(w.H):
+            q_lat = q_nope[i, h] @ W_uk[h]  # [1, R]
+            s = scale * (q_lat @ rows[:, :w.R].T + q_pe[i, h] @ rows[:, w.R:].T)
+            e = np.exp(s - s.max())
+            P = e / e.sum()
+            O[i, h] = (P @ rows[:, :w.R]) @ W_uv[h].T
     return O

@@ -200,3 +200,79 @@ def test_generator_reproducible():
     assert abs(float(x["W"].float().std()) - 512 ** -0.5) < 1e-3
     assert abs(float(x["gain"].float().mean()) - 1.0) < 0.05
     assert abs(float(x["gain"].float().std()) - 0.1 ** 0.5) < 0.03
+
+
+# ---- decode against a compressed-latent cache (normalised latent + rotated
+# rotary key per token, re-expanded on every call)
+
+def _tiny_latent(seed, L=9, q_pos=8, pairing="half", rope=workloads.YARN_KIMI, B=2):
+    return workloads.custom(name="tinylat", B=B, T=1, H=2, R=16, Dn=8, Dr=4, Dv=6, seed=seed, decode=True,
+                            cache_len=L, q_pos=q_pos, pairing=pairing, rope=rope, latent_cache=True)
+
+
+@pytest.mark.parametrize("args,q_pos", [
+    (dict(seed=31), None),
+    (dict(seed=32, L=12, q_pos=11, pairing="interleaved"), None),
+    (dict(seed=33, L=10, q_pos=9, B=3), [0, 4, 9]),  # ragged: one sequence sees only its new row
+])
+def test_decode_latent_matches_brute_force(args, q_pos):
+    w = _tiny_latent(**args)
+    inp = workloads.make_inputs(w)
+    assert inp["latent_cache"].dtype == torch.float16
+    np.testing.assert_allclose(O.decode_latent(w, inp, q_pos=q_pos), np.array(brute.decode_latent(w, inp, q_pos)),
+                               rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("q_pos", [None, [36, 0, 17]])
+def test_decode_latent_equals_absorbed(q_pos):
+    w = workloads.WORKLOADS["tiny_decode_latent"]
+    inp = workloads.make_inputs(w)
+    e = O.decode_latent(w, inp, q_pos=q_pos)
+    a = O.decode_latent_absorbed(w, inp, q_pos=q_pos)
+    np.testing.assert_allclose(a, e, rtol=1e-10, atol=1e-12)
+
+
+def test_decode_latent_single_row_closed_form():
+    # A query at position 0 sees only its own row: softmax of one score is 1,
+    # so the output is that row's value, W_uv times the normalised latent.
+    w = _tiny_latent(seed=34, L=5, q_pos=4)
+    inp = workloads.make_inputs(w)
+    out = O.decode_latent(w, inp, q_pos=[0, 0])
+    c = O.rmsnorm(inp["latent"].double().numpy(), inp["gain"].double().numpy(), w.eps)[:, 0]  # [B,R]
+    Wv = inp["W"].double().numpy().reshape(w.H, w.Dn + w.Dv, w.R)[:, w.Dn:]  # [H,Dv,R]
+    ref = np.einsum("hjr,br->bhj", Wv, c)
+    np.testing.assert_allclose(out[:, :, 0], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_decode_latent_equals_expanded_cache_decode():
+    # Expanding every cached latent row into per-head keys/values (with the
+    # shared rotated rotary key broadcast) and running the expanded-cache
+    # decode gives the same output.
+    w = _tiny_latent(seed=35, L=11, q_pos=10)
+    inp = workloads.make_inputs(w)
+    cache = inp["latent_cache"].double().numpy()
+    k_nope, v = O.kv_expand(cache[:, :, :w.R], inp["W"].double().numpy(), w.H, w.Dn, w.Dv)
+    k_cache = np.concatenate([k_nope, np.broadcast_to(cache[:, None, :, w.R:], k_nope.shape[:3] + (w.Dr,))], -1)
+    wd = dataclasses.replace(w, latent_cache=False)
+    dinp = {k: inp[k] for k in ("q", "latent", "k_pe", "gain", "W")}
+    dinp["k_cache"] = torch.from_numpy(k_cache.copy())
+    dinp["v_cache"] = torch.from_numpy(v.copy())
+    np.testing.assert_allclose(O.decode_latent(w, inp), O.decode(wd, dinp), rtol=1e-12, atol=1e-13)
+
+
+def test_decode_latent_equals_prefill_last_row():
+    # A latent cache filled with what a prefill over the same tokens
+    # normalises and rotates gives, at the last position, the prefill's last
+    # output row.
+    T = 9
+    wp = workloads.custom(B=2, T=T, H=2, R=16, Dn=8, Dr=4, Dv=6, seed=36, rope=workloads.YARN_KIMI)
+    inp = workloads.make_inputs(wp)
+    ref = O.prefill(wp, inp)
+    parts = O.prefill_parts(wp, inp)
+    wd = dataclasses.replace(wp, T=1, decode=True, cache_len=T, q_pos=T - 1, latent_cache=True)
+    cache = np.concatenate([parts["c_norm"], parts["k_pe"]], -1)
+    cache[:, T - 1] = 99.0  # slot T-1 is overwritten by the step
+    dinp = {"q": inp["q"][:, :, T - 1:T], "latent": inp["latent"][:, T - 1:T], "k_pe": inp["k_pe"][:, T - 1:T],
+            "gain": inp["gain"], "W": inp["W"], "latent_cache": torch.from_numpy(cache)}
+    out = O.decode_latent(wd, dinp)
+    np.testing.assert_allclose(out[:, :, 0], ref[:, :, T - 1], rtol=1e-12, atol=1e-13)

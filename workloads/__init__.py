@@ -15,12 +15,19 @@ compressed latent and the single rotary key shared by all heads (first page,
 compression"), the latent RMSNorm gain and the kv_b_proj weight stored as an
 nn.Linear weight of shape [H*(Dn+Dv), R].
 
+Two further decode workloads (a tiny one and a Kimi-K2-shape one) keep a
+compressed-latent cache instead of the expanded one: per token the
+normalised latent followed by the rotated shared rotary key (GLM-5
+"Normalized key-value latent", section "KV cache"), stored as float16, the
+type the latent RMSNorm writes.
+
 Distribution notation N(mu, s2) is read as mean and variance. The RMSNorm
 gain 1 + N(0, 0.1) is given for the tiny workload only and is reused for the
 others. Draw order per workload: q, latent, k_pe, gain, W, then (decode) the K
-cache and the V cache. Every draw is a float32 standard normal from a CPU
-torch.Generator seeded with the workload's seed, scaled, then rounded to
-bfloat16 (round to nearest even).
+cache and the V cache, or the latent cache. Every draw is a float32 standard
+normal from a CPU torch.Generator seeded with the workload's seed, scaled,
+then rounded to bfloat16 (round to nearest even); the latent cache's draws
+are rounded to float16 instead.
 """
 
 from __future__ import annotations
@@ -64,6 +71,7 @@ class Workload:
     decode: bool = False
     cache_len: int = 0  # decode: number of cached rows including the new one
     q_pos: int = 0  # decode: position of the new token
+    latent_cache: bool = False  # decode: the cache holds latents, not expanded keys/values
 
     @property
     def Dqk(self) -> int:
@@ -90,6 +98,12 @@ WORKLOADS = {
     "kimi_k2_decode": Workload("kimi_k2_decode", B=32, T=1, H=64, R=512, Dn=128, Dr=64, Dv=128,
                                rope=YARN_KIMI, pairing="half", seed=4, decode=True,
                                cache_len=1001, q_pos=1000),
+    "tiny_decode_latent": Workload("tiny_decode_latent", B=3, T=1, H=4, R=64, Dn=32, Dr=16, Dv=32,
+                                   rope=RopeSpec(kind="default", base=10000.0), pairing="half", seed=6,
+                                   decode=True, cache_len=37, q_pos=36, latent_cache=True),
+    "kimi_k2_decode_latent": Workload("kimi_k2_decode_latent", B=32, T=1, H=64, R=512, Dn=128, Dr=64, Dv=128,
+                                      rope=YARN_KIMI, pairing="half", seed=5, decode=True,
+                                      cache_len=1001, q_pos=1000, latent_cache=True),
 }
 
 ORDER = ["tiny", "kimi_k2_1k", "kimi_k2_8k", "glm5_4k", "kimi_k2_decode"]
@@ -128,7 +142,10 @@ def make_inputs(w: Workload, with_cache: bool = True, device: str = "cpu") -> di
     and for a decode workload, also
       k_cache [B, H, L, Dn+Dr]  expanded key cache, rotary part already rotated
       v_cache [B, H, L, Dv]     expanded value cache
-    where the new token's row (slot q_pos) of both caches is the one the
+    or, for a latent-cache decode workload,
+      latent_cache [B, L, R+Dr] float16: normalised latent, then the rotated
+                                shared rotary key
+    where the new token's row (slot q_pos) of the cache(s) is the one the
     decode step overwrites.
     """
     gen = torch.Generator(device=device)
@@ -140,7 +157,10 @@ def make_inputs(w: Workload, with_cache: bool = True, device: str = "cpu") -> di
         "gain": _normal(gen, (w.R,), std=math.sqrt(0.1), mean=1.0),
         "W": _normal(gen, (w.H * (w.Dn + w.Dv), w.R), std=1.0 / math.sqrt(w.R)),
     }
-    if w.decode and with_cache:
+    if w.decode and with_cache and w.latent_cache:
+        x = torch.randn(w.B, w.cache_len, w.R + w.Dr, generator=gen, dtype=torch.float32, device=gen.device)
+        out["latent_cache"] = x.to(torch.float16)
+    elif w.decode and with_cache:
         out["k_cache"] = _normal(gen, (w.B, w.H, w.cache_len, w.Dqk))
         out["v_cache"] = _normal(gen, (w.B, w.H, w.cache_len, w.Dv))
     return out
