@@ -17,7 +17,8 @@ from ._lib import DTYPE_BF16, DTYPE_FP16, PAIR_HALF, PAIR_INTERLEAVED, ROPE_DEFA
 
 __all__ = [
     "RopeParams", "rope_params", "mla_rope_table_build", "mla_softmax_scale", "mla_latent_rmsnorm",
-    "mla_kv_expand", "mla_prefill_attention", "mla_decode_attention", "pairing_code",
+    "mla_kv_expand", "mla_prefill_attention", "mla_decode_attention", "mla_absorb_prepare",
+    "mla_latent_cache_append", "mla_decode_absorbed", "pairing_code",
     "PAIR_HALF", "PAIR_INTERLEAVED", "ROPE_DEFAULT", "ROPE_YARN",
 ]
 
@@ -280,4 +281,96 @@ def mla_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     have = ctypes.c_size_t(workspace.numel())
     check("mla_decode_attention",
           lib.mla_decode_attention(*head, _ptr(workspace), ctypes.byref(have), _ptr(out), _stream(q)))
+    return out
+
+
+# ---- decode against a compressed-latent cache (absorbed form)
+
+def mla_absorb_prepare(W: torch.Tensor, H: int, Dn: int, Dv: int,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """W_uk transposed per head, [H, R, Dn] bf16, from the kv_b_proj weight
+    W [H*(Dn+Dv), R] (one-time weight preparation for mla_decode_absorbed)."""
+    _need(W, "W")
+    R = W.shape[1]
+    _shape(W, "W", (H * (Dn + Dv), R))
+    if out is None:
+        out = torch.empty((H, R, Dn), dtype=torch.bfloat16, device=W.device)
+    _need(out, "out")
+    _shape(out, "out", (H, R, Dn))
+    check("mla_absorb_prepare", _lib.load().mla_absorb_prepare(_ptr(W), H, R, Dn, Dv, _ptr(out), _stream(W)))
+    return out
+
+
+def mla_latent_cache_append(latent: torch.Tensor, gain: torch.Tensor, k_pe: torch.Tensor, cos: torch.Tensor,
+                            sin: torch.Tensor, t_pos: torch.Tensor, cache: torch.Tensor, eps: float = 1e-6,
+                            pairing="half") -> torch.Tensor:
+    """Write each sequence's new token into row t_pos[b] of the latent cache
+    [B, Lcap, R+Dr] fp16: its normalised latent, then its rotary key rotated
+    at that position. latent [B, R] and k_pe [B, Dr] are bf16."""
+    _need(latent, "latent")
+    _need(gain, "gain")
+    _need(k_pe, "k_pe")
+    _need(cos, "cos", torch.float32)
+    _need(sin, "sin", torch.float32)
+    _need(t_pos, "t_pos", torch.int32)
+    _need(cache, "cache", torch.float16)
+    B, R = latent.shape
+    Dr = k_pe.shape[-1]
+    _shape(gain, "gain", (R,))
+    _shape(k_pe, "k_pe", (B, Dr))
+    _shape(t_pos, "t_pos", (B,))
+    _shape(sin, "sin", cos.shape)
+    if cache.dim() != 3 or cache.shape[0] != B or cache.shape[2] != R + Dr:
+        raise ValueError(f"cache should be [{B}, Lcap, {R + Dr}], but is {tuple(cache.shape)}")
+    if cos.dim() != 2 or cos.shape[1] != Dr // 2:
+        raise ValueError(f"cos should be [table_len, {Dr // 2}], but is {tuple(cos.shape)}")
+    check("mla_latent_cache_append",
+          _lib.load().mla_latent_cache_append(_ptr(latent), _ptr(gain), float(eps), _ptr(k_pe), _ptr(cos), _ptr(sin),
+                                              cos.shape[0], _ptr(t_pos), pairing_code(pairing), B, R, Dr,
+                                              _ptr(cache), cache.shape[1], _stream(latent)))
+    return cache
+
+
+def mla_decode_absorbed(q: torch.Tensor, W: torch.Tensor, w_ukt: torch.Tensor, cache: torch.Tensor,
+                        seq_len: torch.Tensor, q_pos: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor,
+                        scale: float, Dn: int, Dv: int, pairing="half", num_splits: int = 0,
+                        out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention out [B, H, 1, Dv] bf16 of q [B, H, 1, Dn+Dr] against
+    the latent cache [B, Lcap, R+Dr] fp16, by the absorbed form (W_uk folded
+    into the query, W_uv applied to the attention-weighted latent)."""
+    _need(q, "q")
+    _need(W, "W")
+    _need(w_ukt, "w_ukt")
+    _need(cache, "cache", torch.float16)
+    _need(seq_len, "seq_len", torch.int32)
+    _need(q_pos, "q_pos", torch.int32)
+    _need(cos, "cos", torch.float32)
+    _need(sin, "sin", torch.float32)
+    B, H, _, Dqk = q.shape
+    Dr = Dqk - Dn
+    Lcap, RW = cache.shape[1], cache.shape[2]
+    R = RW - Dr
+    _shape(q, "q", (B, H, 1, Dqk))
+    _shape(W, "W", (H * (Dn + Dv), R))
+    _shape(w_ukt, "w_ukt", (H, R, Dn))
+    _shape(cache, "cache", (B, Lcap, R + Dr))
+    _shape(seq_len, "seq_len", (B,))
+    _shape(q_pos, "q_pos", (B,))
+    _shape(sin, "sin", cos.shape)
+    if cos.dim() != 2 or cos.shape[1] != Dr // 2:
+        raise ValueError(f"cos should be [table_len, {Dr // 2}], but is {tuple(cos.shape)}")
+    if out is None:
+        out = torch.empty((B, H, 1, Dv), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out")
+    _shape(out, "out", (B, H, 1, Dv))
+    lib = _lib.load()
+    head = (_ptr(q), _ptr(W), _ptr(w_ukt), _ptr(cache), _ptr(seq_len), _ptr(q_pos), _ptr(cos), _ptr(sin),
+            cos.shape[0], B, H, Lcap, R, Dn, Dr, Dv, float(scale), pairing_code(pairing), int(num_splits))
+    need = ctypes.c_size_t(0)
+    check("mla_decode_absorbed", lib.mla_decode_absorbed(*head, None, ctypes.byref(need), _ptr(out), _stream(q)))
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty((need.value,), dtype=torch.uint8, device=q.device)
+    have = ctypes.c_size_t(workspace.numel())
+    check("mla_decode_absorbed",
+          lib.mla_decode_absorbed(*head, _ptr(workspace), ctypes.byref(have), _ptr(out), _stream(q)))
     return out

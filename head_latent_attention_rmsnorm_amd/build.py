@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmla.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["rope_table.hip", "rmsnorm.hip", "kv_expand.hip", "prefill_attn.hip", "decode_attn.hip", "api.cpp"]
+SOURCES = ["rope_table.hip", "rmsnorm.hip", "kv_expand.hip", "prefill_attn.hip", "decode_attn.hip", "decode_latent.hip",
+           "api.cpp"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -256,4 +256,105 @@ mla_status mla_decode_attention(const mla_bf16* q, const uint16_t* k_cache, cons
   return hip_status(mla::launch_decode(a, stream));
 }
 
+// ---- decode against a compressed-latent cache (absorbed form)
+
+mla_status mla_absorb_prepare(const mla_bf16* W, int32_t H, int32_t R, int32_t Dn, int32_t Dv, mla_bf16* w_ukt,
+                              hipStream_t stream) {
+  if (H < 1 || H > 65535 || R < 1 || R > 8192 || Dn < 1 || Dn > 512 || Dv < 0 || Dv > 512) return MLA_ERR_SHAPE;
+  if ((int64_t)H * (Dn + Dv) * R > kMaxElems) return MLA_ERR_SHAPE;
+  if (!W || !w_ukt) return MLA_ERR_NULL;
+  clear_stale_error();
+  return hip_status(mla::launch_absorb_prepare(W, w_ukt, H, R, Dn, Dv, stream));
+}
+
+mla_status mla_latent_cache_append(const mla_bf16* latent, const mla_bf16* gain, float eps, const mla_bf16* k_pe,
+                                   const float* cos, const float* sin, int32_t table_len, const int32_t* t_pos,
+                                   int32_t pairing, int32_t B, int32_t R, int32_t Dr, uint16_t* cache, int32_t Lcap,
+                                   hipStream_t stream) {
+  if (B < 0 || R < 1 || R > 8192 || Dr < 2 || Dr > 256 || (Dr & 1) || Lcap < 1) return MLA_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return MLA_ERR_SHAPE;
+  if (!pairing_ok(pairing)) return MLA_ERR_ROPE_TYPE;
+  if ((int64_t)B * Lcap * (R + Dr) > kMaxElems) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!latent || !gain || !k_pe || !cos || !sin || !t_pos || !cache) return MLA_ERR_NULL;
+  if (table_len < 1) return MLA_ERR_SHAPE;
+  clear_stale_error();
+  mla::LatentAppendArgs a{latent, gain, eps, k_pe, cos, sin, table_len, t_pos, pairing, B, R, Dr, Lcap, cache};
+  return hip_status(mla::launch_latent_append(a, stream));
+}
+
+namespace {
+struct AbsorbedPlan {
+  int S, tps;
+  size_t qa_bytes, po_bytes, lse_bytes, ol_bytes;
+  size_t total() const { return qa_bytes + po_bytes + lse_bytes + ol_bytes; }
+};
+// Splits over the key axis: enough workgroups for the chip (about 256)
+// when the batch is small, each split a whole number of 64-key tiles.
+AbsorbedPlan absorbed_plan(int32_t B, int32_t H, int32_t Lcap, int32_t num_splits) {
+  AbsorbedPlan p{};
+  const int tiles = (Lcap + 63) / 64;
+  int S = num_splits;
+  if (S == 0) {
+    const int64_t groups = (int64_t)B * ((H + 63) / 64);
+    S = (int)((256 + groups - 1) / (groups > 0 ? groups : 1));
+  }
+  S = S < 1 ? 1 : S;
+  S = S > mla::kMaxLatentSplits ? mla::kMaxLatentSplits : S;
+  S = S > tiles ? tiles : S;
+  p.tps = (tiles + S - 1) / S;
+  p.S = (tiles + p.tps - 1) / p.tps;
+  p.qa_bytes = round256((size_t)B * H * (mla::kLatentR + mla::kLatentDr) * 2);
+  p.po_bytes = round256((size_t)B * p.S * H * mla::kLatentR * 2);
+  p.lse_bytes = round256((size_t)B * p.S * H * 4);
+  p.ol_bytes = round256((size_t)B * H * mla::kLatentR * 2);
+  return p;
+}
+}  // namespace
+
+mla_status mla_decode_absorbed(const mla_bf16* q, const mla_bf16* W, const mla_bf16* w_ukt, const uint16_t* cache,
+                               const int32_t* seq_len, const int32_t* q_pos, const float* cos, const float* sin,
+                               int32_t table_len, int32_t B, int32_t H, int32_t Lcap, int32_t R, int32_t Dn,
+                               int32_t Dr, int32_t Dv, float scale, int32_t pairing, int32_t num_splits,
+                               void* workspace, size_t* ws_bytes, mla_bf16* out, hipStream_t stream) {
+  if (B < 0 || B > 65535 || H < 1 || H > 65535 || Lcap < 1) return MLA_ERR_SHAPE;
+  if (R != mla::kLatentR || Dr != mla::kLatentDr) return MLA_ERR_UNSUPPORTED;
+  if (Dn < 16 || Dn > 512 || (Dn % 16) || Dv < 32 || Dv > 512 || (Dv % 32)) return MLA_ERR_UNSUPPORTED;
+  if (!pairing_ok(pairing)) return MLA_ERR_ROPE_TYPE;
+  if (num_splits < 0 || num_splits > mla::kMaxLatentSplits) return MLA_ERR_SHAPE;
+  if ((int64_t)Lcap * (R + Dr) * 2 >= ((int64_t)1 << 31)) return MLA_ERR_SHAPE;  // one sequence's cache < 2 GiB
+  if ((int64_t)B * Lcap * (R + Dr) > kMaxElems || (int64_t)B * H * R > kMaxElems) return MLA_ERR_SHAPE;
+  const AbsorbedPlan plan = absorbed_plan(B, H, Lcap, num_splits);
+  const size_t need = plan.total();
+  if (!workspace && ws_bytes) {
+    *ws_bytes = need;
+    return MLA_OK;
+  }
+  if (!(scale > 0.0f) || !isfinite(scale)) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!q || !W || !w_ukt || !cache || !seq_len || !q_pos || !cos || !sin || !out) return MLA_ERR_NULL;
+  if (table_len < 1) return MLA_ERR_SHAPE;
+  if (!workspace || (ws_bytes && *ws_bytes < need)) return MLA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(W) || !aligned16(w_ukt) || !aligned16(cache) || !aligned16(workspace))
+    return MLA_ERR_SHAPE;
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* qa = reinterpret_cast<uint16_t*>(ws);
+  uint16_t* part_o = reinterpret_cast<uint16_t*>(ws + plan.qa_bytes);
+  float* part_lse = reinterpret_cast<float*>(ws + plan.qa_bytes + plan.po_bytes);
+  uint16_t* o_lat = reinterpret_cast<uint16_t*>(ws + plan.qa_bytes + plan.po_bytes + plan.lse_bytes);
+  clear_stale_error();
+  const float kLog2e = 1.4426950408889634f;
+  mla::AbsorbArgs aa{q, w_ukt, q_pos, cos, sin, table_len, B, H, Dn, Dr, pairing, scale * kLog2e, qa};
+  hipError_t e = mla::launch_absorb_q(aa, stream);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  mla::LatentAttnArgs la{qa, cache, seq_len, part_o, part_lse, B, H, Lcap, plan.S, plan.tps};
+  e = mla::launch_latent_attn(la, stream);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  mla::LatentCombineArgs ca{part_o, part_lse, o_lat, B, H, plan.S};
+  e = mla::launch_latent_combine(ca, stream);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  mla::UnabsorbArgs ua{o_lat, W, out, B, H, Dn, Dv};
+  return hip_status(mla::launch_unabsorb(ua, stream));
+}
+
 }  // extern "C"

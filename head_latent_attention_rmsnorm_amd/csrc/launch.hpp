@@ -97,4 +97,65 @@ int decode_auto_splits(int B, int H, int Tcap);
 size_t decode_workspace_bytes(int B, int H, int Dv, int splits);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// ---- decode against a compressed-latent cache (absorbed form); the cache
+// row is 576 fp16 values: 512 latent then 64 rotated rotary key
+constexpr int kLatentR = 512;
+constexpr int kLatentDr = 64;
+constexpr int kMaxLatentSplits = 64;
+
+hipError_t launch_absorb_prepare(const uint16_t* W, uint16_t* wt, int H, int R, int Dn, int Dv, hipStream_t stream);
+
+struct LatentAppendArgs {
+  const uint16_t* latent;  // [B, R] bf16
+  const uint16_t* gain;    // [R] bf16
+  float eps;
+  const uint16_t* k_pe;  // [B, Dr] bf16, not rotated
+  const float* cos;
+  const float* sin;
+  int table_len;
+  const int32_t* t_pos;  // [B]: cache row and rotary position
+  int pairing, B, R, Dr, Lcap;
+  uint16_t* cache;  // [B, Lcap, R+Dr] fp16
+};
+hipError_t launch_latent_append(const LatentAppendArgs& a, hipStream_t stream);
+
+struct AbsorbArgs {
+  const uint16_t* q;      // [B, H, 1, Dn+Dr] bf16
+  const uint16_t* w_ukt;  // [H, 512, Dn] bf16
+  const int32_t* q_pos;   // [B]
+  const float* cos;
+  const float* sin;
+  int table_len;
+  int B, H, Dn, Dr, pairing;
+  float qscale;  // scale * log2(e)
+  uint16_t* qa;  // [B, H, 576] fp16
+};
+hipError_t launch_absorb_q(const AbsorbArgs& a, hipStream_t stream);
+
+struct LatentAttnArgs {
+  const uint16_t* qa;      // [B, H, 576] fp16
+  const uint16_t* cache;   // [B, Lcap, 576] fp16
+  const int32_t* seq_len;  // [B]
+  uint16_t* part_o;        // [B, S, H, 512] fp16, normalised per split
+  float* part_lse;         // [B, S, H] log2 domain, -inf for an empty split
+  int B, H, Lcap, S, tps;  // splits, 64-key tiles per split
+};
+hipError_t launch_latent_attn(const LatentAttnArgs& a, hipStream_t stream);
+
+struct LatentCombineArgs {
+  const uint16_t* part_o;
+  const float* part_lse;
+  uint16_t* o_lat;  // [B, H, 512] fp16
+  int B, H, S;
+};
+hipError_t launch_latent_combine(const LatentCombineArgs& a, hipStream_t stream);
+
+struct UnabsorbArgs {
+  const uint16_t* o_lat;  // [B, H, 512] fp16
+  const uint16_t* W;      // [H*(Dn+Dv), 512] bf16
+  uint16_t* out;          // [B, H, 1, Dv] bf16
+  int B, H, Dn, Dv;
+};
+hipError_t launch_unabsorb(const UnabsorbArgs& a, hipStream_t stream);
+
 }  // namespace mla

@@ -2,7 +2,8 @@
  * mla.h - C ABI of the MI355X (gfx950) eager multi-head latent attention
  * forward path: latent RMSNorm -> kv_b_proj expansion -> rotary embedding
  * (default or YaRN) -> causal scaled softmax attention, plus a decode step
- * against an expanded per-head KV cache.
+ * against an expanded per-head KV cache and one against a compressed-latent
+ * cache (absorbed form).
  *
  * Pages cited below:
  *   [eq]        equation page "Read the equation" and its "Original context":
@@ -19,7 +20,9 @@
  *   [GLM-kv]    GLM-5 "Normalized key-value latent", sections "Key-value
  *               compression" and "KV cache": latent RMSNorm with default
  *               epsilon 1e-6, kv_b_proj shape, expand_kv, shared rotary key
- *               broadcast to every head, interleaved rotary variant.
+ *               broadcast to every head, interleaved rotary variant; the
+ *               cache keeps the normalised latent and the rotated rotary
+ *               key per token and re-expands them on every call.
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE memory owned by the caller; the library
@@ -249,6 +252,68 @@ mla_status mla_decode_attention(const mla_bf16* q, const uint16_t* k_cache,
                                 int32_t Dr, int32_t Dv, float scale, int32_t pairing,
                                 int32_t num_splits, void* workspace, size_t* ws_bytes,
                                 mla_bf16* out, hipStream_t stream);
+
+/* ---- Decode against a compressed-latent cache ---------------------------
+ * Cache layout (the "latent cache"): device fp16 [B, Lcap, R+Dr], row s of
+ * sequence b = [ normalised latent of token s (R values) | its rotary key
+ * rotated at position s (Dr values) ] [GLM-kv, "KV cache"].
+ * The output equals the expanded-cache decode with keys
+ * [W_uk[h] c_s | k_s] and values W_uv[h] c_s; the absorbed evaluation
+ * [eq: the absorbed path folds W_uk into the query and applies W_uv after
+ * attention] never forms them. W_uk[h] / W_uv[h] are rows h*(Dn+Dv) ..
+ * +Dn-1 / +Dn .. +Dn+Dv-1 of the kv_b_proj weight W [H*(Dn+Dv), R]. */
+
+/* One-time weight preparation for mla_decode_absorbed: the key half of
+ * kv_b_proj transposed per head, w_ukt[h, r, j] = W[h*(Dn+Dv) + j, r] for
+ * j < Dn (bf16 copy). Args: W device bf16 [H*(Dn+Dv), R]; w_ukt device bf16
+ * [H, R, Dn] (caller-owned, written). 1 <= R <= 8192, 1 <= Dn, Dv <= 512.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_HIP. */
+mla_status mla_absorb_prepare(const mla_bf16* W, int32_t H, int32_t R, int32_t Dn, int32_t Dv, mla_bf16* w_ukt,
+                              hipStream_t stream);
+
+/* Append the new token of each sequence to a latent cache [GLM-kv: the
+ * normalised latent and the rotated key go into the cache]: row t = t_pos[b]
+ * of sequence b becomes [ RMSNorm(latent[b]) with gain and eps (fp32, one
+ * fp16 rounding) | k_pe[b] rotated at position t (fp16) ].
+ * Args: latent device bf16 [B, R]; gain device bf16 [R]; k_pe device bf16
+ * [B, Dr] (not rotated); cos/sin device fp32 [table_len, Dr/2]; t_pos
+ * device int32 [B] (clamped to [0, Lcap-1] for the row and to the table for
+ * the rotation); cache device fp16 [B, Lcap, R+Dr] (only the B rows are
+ * written). B >= 0 (0 is a no-op), 1 <= R <= 8192, Dr even in [2, 256].
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_ROPE_TYPE, MLA_ERR_HIP. */
+mla_status mla_latent_cache_append(const mla_bf16* latent, const mla_bf16* gain, float eps, const mla_bf16* k_pe,
+                                   const float* cos, const float* sin, int32_t table_len, const int32_t* t_pos,
+                                   int32_t pairing, int32_t B, int32_t R, int32_t Dr, uint16_t* cache, int32_t Lcap,
+                                   hipStream_t stream);
+
+/* Decode attention of one new token per sequence against a latent cache, by
+ * the absorbed form [eq; K2-query: scaled softmax attention; GLM-kv]:
+ *   q_lat[b,h] = W_uk[h]^T q[b,h,0,0:Dn]            (R values)
+ *   S[s] = scale * ( q_lat . c_s + rot(q[b,h,0,Dn:], q_pos[b]) . k_s ),
+ *          s < seq_len[b]
+ *   out[b,h,0,:] = W_uv[h] ( sum_s softmax(S)_s c_s )
+ * with (c_s | k_s) = cache[b, s]. Split-K over the key axis: each split
+ * gives a normalised partial latent aggregate and its log-sum-exp, merged
+ * before the W_uv product. The new token must already be in the cache
+ * (mla_latent_cache_append).
+ * Args: q device bf16 [B, H, 1, Dn+Dr]; W device bf16 [H*(Dn+Dv), R];
+ *   w_ukt device bf16 [H, R, Dn] from mla_absorb_prepare; cache device fp16
+ *   [B, Lcap, R+Dr]; seq_len device int32 [B] (clamped to [1, Lcap]); q_pos
+ *   device int32 [B]; cos/sin device fp32 [table_len, Dr/2]; scale from
+ *   mla_softmax_scale (of Dn+Dr); num_splits 0 = automatic, else 1..64 (at
+ *   most one split per 64 cache rows is used); out device bf16 [B, H, 1, Dv].
+ *   workspace/ws_bytes as for mla_prefill_attention (size depends on B, H,
+ *   Lcap and the split count). Pointers to q, W, w_ukt, cache and workspace
+ *   16-byte aligned.
+ *   Supported: R = 512, Dr = 64, Dn a multiple of 16 in [16, 512], Dv a
+ *   multiple of 32 in [32, 512]; Lcap*(R+Dr)*2 < 2^31.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED,
+ *   MLA_ERR_ROPE_TYPE, MLA_ERR_WORKSPACE, MLA_ERR_HIP. */
+mla_status mla_decode_absorbed(const mla_bf16* q, const mla_bf16* W, const mla_bf16* w_ukt, const uint16_t* cache,
+                               const int32_t* seq_len, const int32_t* q_pos, const float* cos, const float* sin,
+                               int32_t table_len, int32_t B, int32_t H, int32_t Lcap, int32_t R, int32_t Dn,
+                               int32_t Dr, int32_t Dv, float scale, int32_t pairing, int32_t num_splits,
+                               void* workspace, size_t* ws_bytes, mla_bf16* out, hipStream_t stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* mla_status_string(mla_status s);

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared()
-    assert len(names) == 7
+    assert len(names) == 10
     assert sorted(_lib.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -166,3 +166,68 @@ def test_decode_validation(lib):
     assert decode(lib, ws=None) == WS
     assert decode(lib, dtype=3) == UNSUP
     assert decode(lib, B=0) == OK
+
+
+def test_absorb_prepare_validation(lib):
+    def call(W=FAKE, H=64, R=512, Dn=128, Dv=128, out=FAKE):
+        return lib.mla_absorb_prepare(W, H, R, Dn, Dv, out, None)
+    assert call(W=None) == NULL
+    assert call(out=None) == NULL
+    assert call(H=0) == SHAPE
+    assert call(R=0) == SHAPE
+    assert call(Dn=0) == SHAPE
+    assert call(Dv=-1) == SHAPE
+    assert call(R=9000) == SHAPE
+
+
+def latent_append(lib, **kw):
+    a = dict(lat=FAKE, gain=FAKE, eps=1e-6, kpe=FAKE, cos=FAKE, sin=FAKE, table_len=1001, tpos=FAKE, pairing=0,
+             B=32, R=512, Dr=64, cache=FAKE, Lcap=1001)
+    a.update(kw)
+    return lib.mla_latent_cache_append(*a.values(), None)
+
+
+def test_latent_append_validation(lib):
+    assert latent_append(lib, B=0) == OK  # empty: no-op
+    assert latent_append(lib, B=0, lat=None, cache=None) == OK
+    assert latent_append(lib, cache=None) == NULL
+    assert latent_append(lib, tpos=None) == NULL
+    assert latent_append(lib, B=-1) == SHAPE
+    assert latent_append(lib, Dr=63) == SHAPE
+    assert latent_append(lib, Lcap=0) == SHAPE
+    assert latent_append(lib, eps=-1.0) == SHAPE
+    assert latent_append(lib, eps=float("nan")) == SHAPE
+    assert latent_append(lib, table_len=0) == SHAPE
+    assert latent_append(lib, pairing=2) == ROPE
+
+
+def absorbed(lib, ws=FAKE, ws_bytes=None, **kw):
+    a = dict(q=FAKE, W=FAKE, wt=FAKE, cache=FAKE, seq=FAKE, qpos=FAKE, cos=FAKE, sin=FAKE, table_len=1001, B=32,
+             H=64, Lcap=1001, R=512, Dn=128, Dr=64, Dv=128, scale=0.13, pairing=0, splits=0)
+    a.update(kw)
+    return lib.mla_decode_absorbed(*a.values(), ws, ws_bytes, FAKE, None)
+
+
+def test_decode_absorbed_validation(lib):
+    need = ctypes.c_size_t(0)
+    assert absorbed(lib, ws=None, ws_bytes=ctypes.byref(need)) == OK
+    # absorbed query [B,H,576] fp16 + (B, split, H) partial latent rows fp16 + lse
+    assert need.value >= 32 * 64 * 576 * 2 + 32 * 64 * (512 * 2 + 4)
+    small = ctypes.c_size_t(need.value - 256)
+    assert absorbed(lib, ws_bytes=ctypes.byref(small)) == WS
+    assert absorbed(lib, ws=None) == WS
+    assert absorbed(lib, B=0) == OK
+    assert absorbed(lib, cache=None) == NULL
+    assert absorbed(lib, wt=None) == NULL
+    assert absorbed(lib, R=256) == UNSUP
+    assert absorbed(lib, Dr=32) == UNSUP
+    assert absorbed(lib, Dn=100) == UNSUP
+    assert absorbed(lib, Dv=48) == UNSUP
+    assert absorbed(lib, pairing=5) == ROPE
+    assert absorbed(lib, splits=65) == SHAPE
+    assert absorbed(lib, splits=-1) == SHAPE
+    assert absorbed(lib, Lcap=0) == SHAPE
+    assert absorbed(lib, Lcap=4_000_000) == SHAPE  # one sequence's cache >= 2 GiB
+    assert absorbed(lib, scale=0.0) == SHAPE
+    assert absorbed(lib, table_len=0) == SHAPE
+    assert absorbed(lib, cache=FAKE + 8) == SHAPE  # not 16-byte aligned
