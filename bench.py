@@ -5,7 +5,10 @@ One step = one pass of the whole hot path:
     cos/sin table -> latent RMSNorm -> kv_b_proj expansion -> causal attention
   decode (Kimi-K2 shape, B=32 sequences at position 1000, 1001 cached rows):
     latent RMSNorm -> kv_b_proj expansion appended into the expanded cache ->
-    split-K decode attention.
+    split-K decode attention;
+  decode against a compressed-latent cache (same shape, 576 fp16 values per
+    cached token): RMSNorm + rotary key into the cache row -> absorbed
+    split-K attention (W_uk folded into the query, W_uv after the merge).
 Inputs are drawn on the GPU (same seeded recipe as the parity tests) and are
 resident in HBM before the timed region starts.
 
@@ -16,6 +19,7 @@ Reported (one JSON line):
                   its mean launch time (HIP events on the launch stream)
                   against the MI355X dense 16-bit MFMA peak
   decode          decode attention GB/s (algorithmic bytes) and HBM fraction
+  decode_latent   step time of the latent-cache decode and its attention
   cpu_baseline    the fp64 CPU oracle on a bounded sample (--cpu-baseline)
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -35,6 +39,7 @@ MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 PREFILL = "kimi_k2_8k"
 DECODE = "kimi_k2_decode"
+DECODE_LATENT = "kimi_k2_decode_latent"
 
 
 def log(*a):
@@ -150,6 +155,14 @@ def main():
     out_dec = torch.empty((wd.B, wd.H, 1, wd.Dv), dtype=torch.bfloat16, device=dev)
     splits = args.splits or 0
     ws_dec = torch.empty((max(1, 64 << 20),), dtype=torch.uint8, device=dev)
+    wl = workloads.WORKLOADS[DECODE_LATENT]
+    il = workloads.make_inputs(wl, device=dev)
+    rope_l = mla.api.params_from(wl.rope, wl.Dr)
+    w_ukt = mla.api.mla_absorb_prepare(il["W"], wl.H, wl.Dn, wl.Dv)  # weight preparation, once
+    seq_l = torch.full((wl.B,), wl.cache_len, dtype=torch.int32, device=dev)
+    qpos_l = torch.full((wl.B,), wl.q_pos, dtype=torch.int32, device=dev)
+    out_lat = torch.empty((wl.B, wl.H, 1, wl.Dv), dtype=torch.bfloat16, device=dev)
+    ws_lat = torch.empty((64 << 20,), dtype=torch.uint8, device=dev)
 
     if args.calib_copy_mib:
         src = torch.empty((args.calib_copy_mib << 20,), dtype=torch.uint8, device=dev).fill_(1)
@@ -161,7 +174,7 @@ def main():
         del src, dst
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    rec = {"prefill": [], "attn": [], "decode": [], "dec_attn": []}
+    rec = {"prefill": [], "attn": [], "decode": [], "dec_attn": [], "lat": [], "lat_attn": []}
 
     def step(timed: bool):
         e = [ev() for _ in range(8)] if timed else None
@@ -187,6 +200,15 @@ def main():
                                      tdec.scale, wd.Dn, wd.pairing, splits, out=out_dec, workspace=ws_dec)
         if timed:
             e[4].record()
+        tlat = mla.pipeline.build_table(rope_l, wl.cache_len, wl.Dqk, dev)
+        mla.api.mla_latent_cache_append(il["latent"].view(wl.B, wl.R), il["gain"], il["k_pe"].view(wl.B, wl.Dr),
+                                        tlat.cos, tlat.sin, qpos_l, il["latent_cache"], wl.eps, wl.pairing)
+        if timed:
+            e[5].record()
+        mla.api.mla_decode_absorbed(il["q"], il["W"], w_ukt, il["latent_cache"], seq_l, qpos_l, tlat.cos, tlat.sin,
+                                    tlat.scale, wl.Dn, wl.Dv, wl.pairing, 0, out=out_lat, workspace=ws_lat)
+        if timed:
+            e[6].record()
         return e
 
     log(f"[bench] warmup {args.warmup} steps")
@@ -206,19 +228,25 @@ def main():
         rec["attn"].append(e[1].elapsed_time(e[2]))
         rec["decode"].append(e[2].elapsed_time(e[4]))
         rec["dec_attn"].append(e[3].elapsed_time(e[4]))
+        rec["lat"].append(e[4].elapsed_time(e[6]))
+        rec["lat_attn"].append(e[5].elapsed_time(e[6]))
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
     ms_step = wall * 1e3 / args.steps
     t_prefill = mean(rec["prefill"]) * 1e-3
     t_attn = mean(rec["attn"]) * 1e-3
     t_dec_attn = mean(rec["dec_attn"]) * 1e-3
     t_decode = mean(rec["decode"]) * 1e-3
+    t_lat = mean(rec["lat"]) * 1e-3
+    t_lat_attn = mean(rec["lat_attn"]) * 1e-3
+    lat_bytes = wl.B * wl.cache_len * (wl.R + wl.Dr) * 2  # the latent cache rows read
     fa, fe = attn_flops(wp), expand_flops(wp)
     value = (fa + fe) / t_prefill / 1e12
     attn_tflops = fa / t_attn / 1e12
     dec_gbs = decode_bytes(wd) / t_dec_attn / 1e9
     log(f"[bench] prefill path {t_prefill * 1e3:.3f} ms ({value:.1f} TFLOP/s), attention {t_attn * 1e3:.3f} ms "
         f"({attn_tflops:.1f} TFLOP/s, {attn_tflops / MFMA_PEAK_TFLOPS:.1%} of peak); decode step "
-        f"{t_decode * 1e6:.1f} us, decode attention {t_dec_attn * 1e6:.1f} us ({dec_gbs:.0f} GB/s)")
+        f"{t_decode * 1e6:.1f} us, decode attention {t_dec_attn * 1e6:.1f} us ({dec_gbs:.0f} GB/s); latent-cache "
+        f"decode step {t_lat * 1e6:.1f} us (attention {t_lat_attn * 1e6:.1f} us)")
 
     result = {
         "metric": "MLA prefill attn TFLOP/s + % bf16 MFMA peak; decode GB/s at 1k ctx",
@@ -249,6 +277,14 @@ def main():
             "decode_traffic_bytes": measured_traffic("head_latent_attention_rmsnorm_amd/csrc/decode_attn.hip",
                                                      "decode"),
             "decode_algorithmic_bytes": int(decode_bytes(wd)),
+            "decode_latent_workload": f"{DECODE_LATENT} (B=32 L=1001 pos 1000, fp16 latent cache 576/token)",
+            "decode_latent_step_us": round(t_lat * 1e6, 2),
+            "decode_latent_attention_us": round(t_lat_attn * 1e6, 2),
+            "decode_latent_tokens_per_s": round(wl.B / t_lat, 1),
+            "decode_latent_cache_bytes": int(lat_bytes),
+            "decode_latent_cache_gbs": round(lat_bytes / t_lat_attn / 1e9, 1),
+            "decode_latent_attn_kernel_traffic_bytes": measured_traffic(
+                "head_latent_attention_rmsnorm_amd/csrc/decode_latent.hip", "decode_latent"),
         },
         "roofline": {
             "kernel": "prefill_kernel (causal flash attention, Dqk 192, Dv 128)",
