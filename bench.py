@@ -20,6 +20,9 @@ Reported (one JSON line):
                   against the MI355X dense 16-bit MFMA peak
   decode          decode attention GB/s (algorithmic bytes) and HBM fraction
   decode_latent   step time of the latent-cache decode and its attention
+  chunked         prefill against a past cache: the last 1024-token chunk of
+                  the 8k sequence attending to its 7168 cached rows (timed
+                  after the steps, attention call only)
   cpu_baseline    the fp64 CPU oracle on a bounded sample (--cpu-baseline)
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -231,6 +234,33 @@ def main():
         rec["lat"].append(e[4].elapsed_time(e[6]))
         rec["lat_attn"].append(e[5].elapsed_time(e[6]))
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+
+    # chunked prefill: fill the expanded cache with the whole sequence (the
+    # chunk's own rows included), then time the chunk's attention call
+    TQ = 1024
+    past = wp.T - TQ
+    tab = mla.pipeline.build_table(rope_p, wp.T, wp.Dqk, dev)
+    mla.api.mla_latent_rmsnorm(ip["latent"], ip["gain"], wp.eps, out=bufs.c_norm)
+    mla.api.mla_kv_expand(bufs.c_norm, ip["W"], wp.H, wp.Dn, wp.Dv, k=bufs.k_nope, v=bufs.v, v_layout="cols")
+    k_rot = torch.empty((wp.B, wp.T, wp.Dr), dtype=torch.float16, device=dev)
+    mla.api.mla_rotate_rope_key(ip["k_pe"], tab.cos, tab.sin, k_rot, 0, wp.pairing)
+    q_chunk = ip["q"][:, :, past:].contiguous()
+    out_chunk = torch.empty((wp.B, wp.H, TQ, wp.Dv), dtype=torch.bfloat16, device=dev)
+
+    def chunk():
+        mla.api.mla_prefill_attention_cached(q_chunk, bufs.k_nope, k_rot, bufs.v, past, tab.cos, tab.sin, tab.scale,
+                                             wp.pairing, out=out_chunk)
+    for _ in range(2):
+        chunk()
+    torch.cuda.synchronize()
+    ce = [ev() for _ in range(11)]
+    ce[0].record()
+    for i in range(10):
+        chunk()
+        ce[i + 1].record()
+    torch.cuda.synchronize()
+    t_chunk = mean([ce[i].elapsed_time(ce[i + 1]) for i in range(10)]) * 1e-3
+    chunk_flops = 2.0 * wp.B * wp.H * (TQ * past + TQ * (TQ + 1) / 2) * (wp.Dqk + wp.Dv)
     ms_step = wall * 1e3 / args.steps
     t_prefill = mean(rec["prefill"]) * 1e-3
     t_attn = mean(rec["attn"]) * 1e-3
@@ -246,7 +276,8 @@ def main():
     log(f"[bench] prefill path {t_prefill * 1e3:.3f} ms ({value:.1f} TFLOP/s), attention {t_attn * 1e3:.3f} ms "
         f"({attn_tflops:.1f} TFLOP/s, {attn_tflops / MFMA_PEAK_TFLOPS:.1%} of peak); decode step "
         f"{t_decode * 1e6:.1f} us, decode attention {t_dec_attn * 1e6:.1f} us ({dec_gbs:.0f} GB/s); latent-cache "
-        f"decode step {t_lat * 1e6:.1f} us (attention {t_lat_attn * 1e6:.1f} us)")
+        f"decode step {t_lat * 1e6:.1f} us (attention {t_lat_attn * 1e6:.1f} us); chunked prefill (1024 after "
+        f"7168) {t_chunk * 1e3:.3f} ms ({chunk_flops / t_chunk / 1e12:.1f} TFLOP/s)")
 
     result = {
         "metric": "MLA prefill attn TFLOP/s + % bf16 MFMA peak; decode GB/s at 1k ctx",
@@ -283,6 +314,9 @@ def main():
             "decode_latent_tokens_per_s": round(wl.B / t_lat, 1),
             "decode_latent_cache_bytes": int(lat_bytes),
             "decode_latent_cache_gbs": round(lat_bytes / t_lat_attn / 1e9, 1),
+            "chunked_prefill_workload": f"{PREFILL} last {TQ} tokens after {past} cached rows",
+            "chunked_prefill_attention_ms": round(t_chunk * 1e3, 4),
+            "chunked_prefill_attention_tflops": round(chunk_flops / t_chunk / 1e12, 2),
             "decode_latent_attn_kernel_traffic_bytes": measured_traffic(
                 "head_latent_attention_rmsnorm_amd/csrc/decode_latent.hip", "decode_latent"),
         },

@@ -18,7 +18,8 @@ from ._lib import DTYPE_BF16, DTYPE_FP16, PAIR_HALF, PAIR_INTERLEAVED, ROPE_DEFA
 __all__ = [
     "RopeParams", "rope_params", "mla_rope_table_build", "mla_softmax_scale", "mla_latent_rmsnorm",
     "mla_kv_expand", "mla_prefill_attention", "mla_decode_attention", "mla_absorb_prepare",
-    "mla_latent_cache_append", "mla_decode_absorbed", "pairing_code",
+    "mla_latent_cache_append", "mla_decode_absorbed", "mla_rotate_rope_key", "mla_prefill_attention_cached",
+    "pairing_code",
     "PAIR_HALF", "PAIR_INTERLEAVED", "ROPE_DEFAULT", "ROPE_YARN",
 ]
 
@@ -237,6 +238,71 @@ def mla_prefill_attention(q: torch.Tensor, k_nope: torch.Tensor, k_pe: torch.Ten
     have = ctypes.c_size_t(workspace.numel())
     check("mla_prefill_attention",
           lib.mla_prefill_attention(*args_head, _ptr(workspace), ctypes.byref(have), _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+def mla_rotate_rope_key(k_pe: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor, dst: torch.Tensor, t_off: int = 0,
+                        pairing="half", pos: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rotate k_pe [B, T, Dr] bf16 (at pos [B, T], default t_off + t) into
+    rows t_off.. of the shared rotated-key buffer dst [B, Tcap, Dr] (bf16 or
+    fp16)."""
+    _need(k_pe, "k_pe")
+    _need(cos, "cos", torch.float32)
+    _need(sin, "sin", torch.float32)
+    code = _kv_code(dst, "dst")
+    _need(dst, "dst", dst.dtype)
+    B, T, Dr = k_pe.shape
+    if dst.dim() != 3 or dst.shape[0] != B or dst.shape[2] != Dr:
+        raise ValueError(f"dst should be [{B}, Tcap, {Dr}], but is {tuple(dst.shape)}")
+    _shape(sin, "sin", cos.shape)
+    if pos is not None:
+        _need(pos, "pos", torch.int32)
+        _shape(pos, "pos", (B, T))
+    check("mla_rotate_rope_key",
+          _lib.load().mla_rotate_rope_key(_ptr(k_pe), _ptr(cos), _ptr(sin), cos.shape[0], _ptr(pos), B, T, Dr,
+                                          pairing_code(pairing), _ptr(dst), dst.shape[1], int(t_off), code,
+                                          _stream(k_pe)))
+    return dst
+
+
+def mla_prefill_attention_cached(q: torch.Tensor, k_nope: torch.Tensor, k_rot: torch.Tensor, vt: torch.Tensor,
+                                 past: int, cos: torch.Tensor, sin: torch.Tensor, scale: float, pairing="half",
+                                 pos: Optional[torch.Tensor] = None, return_lse: bool = False,
+                                 out: Optional[torch.Tensor] = None):
+    """Causal attention of the T query tokens q [B, H, T, Dn+Dr] (positions
+    past..past+T-1) against the cache k_nope [B, H, Tcap, Dn], k_rot
+    [B, Tcap, Dr] (rotated) and V^T [B, H, Dv, v_ld], whose rows
+    0..past+T-1 already hold the earlier tokens and the chunk. Returns
+    out [B, H, T, Dv] bf16 (and lse [B, H, T])."""
+    _need(q, "q")
+    code = _kv_code(k_nope, "k_nope")
+    _need(k_nope, "k_nope", k_nope.dtype)
+    _need(k_rot, "k_rot", k_nope.dtype)
+    _need(vt, "vt", k_nope.dtype)
+    _need(cos, "cos", torch.float32)
+    _need(sin, "sin", torch.float32)
+    B, H, T, Dqk = q.shape
+    Tcap, Dn = k_nope.shape[2], k_nope.shape[3]
+    Dr = Dqk - Dn
+    _shape(k_nope, "k_nope", (B, H, Tcap, Dn))
+    _shape(k_rot, "k_rot", (B, Tcap, Dr))
+    if vt.dim() != 4 or tuple(vt.shape[:2]) != (B, H):
+        raise ValueError(f"vt should be [B={B}, H={H}, Dv, v_ld], but is {tuple(vt.shape)}")
+    Dv, v_ld = vt.shape[2], vt.shape[3]
+    _shape(sin, "sin", cos.shape)
+    if out is None:
+        out = torch.empty((B, H, T, Dv), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out")
+    _shape(out, "out", (B, H, T, Dv))
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if return_lse else None
+    if pos is not None:
+        _need(pos, "pos", torch.int32)
+        _shape(pos, "pos", (B, T))
+    check("mla_prefill_attention_cached",
+          _lib.load().mla_prefill_attention_cached(_ptr(q), _ptr(k_nope), _ptr(k_rot), _ptr(vt), v_ld, code,
+                                                   _ptr(cos), _ptr(sin), cos.shape[0], _ptr(pos), B, H, T,
+                                                   int(past), Tcap, Dn, Dr, Dv, float(scale),
+                                                   pairing_code(pairing), _ptr(out), _ptr(lse), _stream(q)))
     return (out, lse) if return_lse else out
 
 

@@ -218,7 +218,51 @@ mla_status mla_prefill_attention(const mla_bf16* q, const uint16_t* k_nope, cons
     vt = vt_ws;
   }
   mla::PrefillArgs a{q, k_nope, k_rot, vt, cos, sin, table_len, pos, out, lse, B, H, T, Dn, Dr, Dv, pairing, scale,
-                     kv_dtype, Tv};
+                     kv_dtype, Tv, 0, T};
+  return hip_status(mla::launch_prefill(a, stream));
+}
+
+mla_status mla_rotate_rope_key(const mla_bf16* k_pe, const float* cos, const float* sin, int32_t table_len,
+                               const int32_t* pos, int32_t B, int32_t T, int32_t Dr, int32_t pairing, uint16_t* dst,
+                               int32_t Tcap, int32_t t_off, int32_t kv_dtype, hipStream_t stream) {
+  if (B < 0 || T < 0 || Dr < 2 || Dr > 256 || (Dr & 1) || Tcap < 1 || t_off < 0) return MLA_ERR_SHAPE;
+  if (!dtype_ok(kv_dtype)) return MLA_ERR_UNSUPPORTED;
+  if (!pairing_ok(pairing)) return MLA_ERR_ROPE_TYPE;
+  if ((int64_t)t_off + T > Tcap || (int64_t)B * Tcap * Dr > kMaxElems) return MLA_ERR_SHAPE;
+  if ((int64_t)B * T == 0) return MLA_OK;
+  if (!k_pe || !cos || !sin || !dst) return MLA_ERR_NULL;
+  if (table_len < 1 || (!pos && (int64_t)t_off + T > table_len)) return MLA_ERR_SHAPE;
+  clear_stale_error();
+  mla::RotKeyArgs r{k_pe, cos, sin, table_len, pos, dst, B, T, 1, Dr, Tcap, t_off, Dr, 0, pairing, kv_dtype};
+  return hip_status(mla::launch_rotate_key(r, stream));
+}
+
+mla_status mla_prefill_attention_cached(const mla_bf16* q, const uint16_t* k_nope, const uint16_t* k_rot,
+                                        const uint16_t* vt, int32_t v_ld, int32_t kv_dtype, const float* cos,
+                                        const float* sin, int32_t table_len, const int32_t* pos, int32_t B,
+                                        int32_t H, int32_t T, int32_t past, int32_t Tcap, int32_t Dn, int32_t Dr,
+                                        int32_t Dv, float scale, int32_t pairing, mla_bf16* out, float* lse,
+                                        hipStream_t stream) {
+  if (B < 0 || H < 1 || T < 0 || past < 0 || Tcap < 1 || Dn < 1 || Dr < 2 || (Dr & 1) || Dv < 1)
+    return MLA_ERR_SHAPE;
+  if (!mla::prefill_supported(Dn + Dr, Dr, Dv) || !dtype_ok(kv_dtype)) return MLA_ERR_UNSUPPORTED;
+  if (!pairing_ok(pairing)) return MLA_ERR_ROPE_TYPE;
+  if ((int64_t)past + T > Tcap || v_ld < (int64_t)past + T || (v_ld % 8)) return MLA_ERR_SHAPE;
+  if ((int64_t)B * H * Tcap * (Dn + Dr) > kMaxElems || (int64_t)B * H * T * (Dn + Dr) > kMaxElems ||
+      (int64_t)B * H > ((int64_t)1 << 24) || (int64_t)Tcap > ((int64_t)1 << 26))
+    return MLA_ERR_SHAPE;
+  // one (b, h) slice of every operand is addressed with 32-bit byte offsets
+  if ((int64_t)Tcap * (Dn > Dv ? Dn : Dv) * 2 > 0x7fffffff || (int64_t)Dv * v_ld * 2 > 0x7fffffff)
+    return MLA_ERR_SHAPE;
+  if (!(scale > 0.0f) || !isfinite(scale)) return MLA_ERR_SHAPE;
+  if ((int64_t)B * T == 0) return MLA_OK;
+  if (!q || !k_nope || !k_rot || !vt || !cos || !sin || !out) return MLA_ERR_NULL;
+  if (table_len < 1 || (!pos && (int64_t)past + T > table_len)) return MLA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_nope) || !aligned16(k_rot) || !aligned16(vt) || !aligned16(out))
+    return MLA_ERR_SHAPE;
+  clear_stale_error();
+  mla::PrefillArgs a{q, k_nope, k_rot, vt, cos, sin, table_len, pos, out, lse, B, H, T, Dn, Dr, Dv, pairing, scale,
+                     kv_dtype, v_ld, past, Tcap};
   return hip_status(mla::launch_prefill(a, stream));
 }
 

@@ -57,9 +57,9 @@ hipError_t launch_rotate_key(const RotKeyArgs& a, hipStream_t stream);
 
 struct PrefillArgs {
   const uint16_t* q;       // [B, H, T, Dqk]
-  const uint16_t* k_nope;  // [B, H, T, Dn]  (kv_dtype)
-  const uint16_t* k_rot;   // [B, T, Dr] rotated (workspace, kv_dtype)
-  const uint16_t* v;       // V^T [B, H, Dv, v_ld] (kv_dtype), columns T..v_ld-1 finite
+  const uint16_t* k_nope;  // [B, H, kv_stride, Dn] (kv_dtype), rows 0..past+T-1 read
+  const uint16_t* k_rot;   // [B, kv_stride, Dr] rotated (kv_dtype)
+  const uint16_t* v;       // V^T [B, H, Dv, v_ld] (kv_dtype), columns past+T..v_ld-1 finite
   const float* cos;
   const float* sin;
   int table_len;
@@ -69,7 +69,9 @@ struct PrefillArgs {
   int B, H, T, Dn, Dr, Dv, pairing;
   float scale;
   int kv_dtype;  // 0 bf16, 1 fp16
-  int v_ld;      // row stride of V^T, a multiple of 8, >= T
+  int v_ld;      // row stride of V^T, a multiple of 8, >= past + T
+  int past;      // cached rows before the T query rows (0 for a plain prefill)
+  int kv_stride; // row capacity of k_nope [B, H, kv_stride, Dn] and k_rot [B, kv_stride, Dr]
 };
 bool prefill_supported(int Dqk, int Dr, int Dv);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

@@ -134,7 +134,10 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
   if (hb >= HB) return;  // padding workgroup: the whole block exits
   const int h = hb % a.H;
   const int b = hb / a.H;
-  const int T = a.T;
+  const int T = a.T;                  // query rows
+  const int past = a.past;            // cached rows before them: query t sits at position past + t
+  const int Tk = past + T;            // key rows
+  const size_t kvs = (size_t)a.kv_stride;  // row capacity of the k_nope / rotated-key buffers
   const size_t bh = (size_t)b * a.H + h;
   const uint16_t* qg = a.q + bh * T * DQK;
 
@@ -154,7 +157,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
     const bool valid = tq < T;
     int p = 0;
     if (valid) {
-      p = a.pos ? a.pos[(size_t)b * T + tq] : tq;
+      p = a.pos ? a.pos[(size_t)b * T + tq] : past + tq;
       p = min(max(p, 0), a.table_len - 1);
     }
     const uint16_t* qrow = qg + (size_t)(valid ? tq : 0) * DQK;
@@ -211,7 +214,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
   }
 
 
-  const int kend = min(T, (qt + 1) * BMW);  // keys [0, kend) are visible to some row
+  const int kend = min(Tk, past + (qt + 1) * BMW);  // keys [0, kend) are visible to some row
   const int nkt = (kend + BN - 1) / BN;
 
   // Key (within a 32-key sub-tile) of operand row r of the S^T MFMA: the
@@ -227,8 +230,8 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
   // as zeros. (Choosing descriptors per tile instead costs tens of scalar
   // instructions per wave, and the 8 waves reach that point together right
   // after the barrier, queueing on the CU's one scalar unit.)
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_nope + bh * T * DN, (uint32_t)T * DN * 2u);
-  const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.k_rot + (size_t)b * T * DR, (uint32_t)T * DR * 2u);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_nope + bh * kvs * DN, (uint32_t)Tk * DN * 2u);
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.k_rot + (size_t)b * kvs * DR, (uint32_t)Tk * DR * 2u);
   const __amdgpu_buffer_rsrc_t rv =
       make_rsrc(a.v + bh * (size_t)DV * a.v_ld, (uint32_t)DV * (uint32_t)a.v_ld * 2u);
   __amdgpu_buffer_rsrc_t rs[LPW];
@@ -306,7 +309,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
     auto vfrag = [&](int d, int s) __attribute__((always_inline)) {
       return *reinterpret_cast<const u32x4*>(sb + (KBLK + d * NPV + (s / SWV) * SWV) * 1024 + rdv[s % SWV]);
     };
-    const bool diag = key0 + BN - 1 > qlo;  // the tile crosses the wave's diagonal
+    const bool diag = key0 + BN - 1 > past + qlo;  // the tile crosses the wave's diagonal
     f32x16 sacc[NSUB];
     u32x4 pf[NPV];
     auto s_chain = [&](int j) __attribute__((always_inline)) {
@@ -328,7 +331,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + j * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
-          if (key > tq) sacc[j][i] = -INFINITY;
+          if (key > past + tq) sacc[j][i] = -INFINITY;
         }
       }
     };
@@ -407,7 +410,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
     const int cur = kt & 1;
     if (kt + 1 < nkt) issue(kt + 1, cur ^ 1);
     const int key0 = kt * BN;
-    if (key0 <= qlo + 31) tile(cur, key0);  // some key of the tile is visible to this wave
+    if (key0 <= past + qlo + 31) tile(cur, key0);  // some key of the tile is visible to this wave
     // the next tile's loads have landed in LDS and every wave is done with
     // this tile's buffer
     __builtin_amdgcn_s_waitcnt(0);

@@ -93,3 +93,35 @@ def decode_latent_step(q, latent, k_pe, gain, W, w_ukt, cache, seq_len, q_pos, t
                                 eps, pairing)
     return api.mla_decode_absorbed(q, W, w_ukt, cache, seq_len, q_pos, table.cos, table.sin, table.scale, Dn, Dv,
                                    pairing, num_splits, out=out, workspace=workspace)
+
+
+@dataclass
+class ChunkCache:
+    """Expanded cache for chunked prefill: k_nope [B, H, Tcap, Dn], the shared
+    rotated rotary key [B, Tcap, Dr] and V^T [B, H, Dv, Tcap] (zero-filled,
+    so columns past the filled rows stay finite)."""
+    k_nope: torch.Tensor
+    k_rot: torch.Tensor
+    vt: torch.Tensor
+
+
+def alloc_chunk_cache(B, H, Tcap, Dn, Dr, Dv, device="cuda", kv_dtype=torch.float16) -> ChunkCache:
+    Tv = (Tcap + 7) // 8 * 8
+    return ChunkCache(torch.zeros((B, H, Tcap, Dn), dtype=kv_dtype, device=device),
+                      torch.zeros((B, Tcap, Dr), dtype=kv_dtype, device=device),
+                      torch.zeros((B, H, Dv, Tv), dtype=kv_dtype, device=device))
+
+
+def prefill_chunk(q, latent, k_pe, gain, W, cache: ChunkCache, past: int, table: RopeTable, pairing="half",
+                  eps: float = 1e-6, return_lse: bool = False, out=None):
+    """One chunk of a chunked prefill: the chunk's tokens (q [B,H,T,Dqk],
+    latent [B,T,R], k_pe [B,T,Dr], positions past..past+T-1) are normalised,
+    expanded and appended to the cache at row `past`, then attend causally
+    to rows 0..past+T-1."""
+    H, Dn = cache.k_nope.shape[1], cache.k_nope.shape[3]
+    Dv = cache.vt.shape[2]
+    c_norm = api.mla_latent_rmsnorm(latent, gain, eps)
+    api.mla_kv_expand(c_norm, W, H, Dn, Dv, k=cache.k_nope, v=cache.vt, v_layout="cols", t_off=past)
+    api.mla_rotate_rope_key(k_pe, table.cos, table.sin, cache.k_rot, past, pairing)
+    return api.mla_prefill_attention_cached(q, cache.k_nope, cache.k_rot, cache.vt, past, table.cos, table.sin,
+                                            table.scale, pairing, return_lse=return_lse, out=out)

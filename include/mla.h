@@ -226,6 +226,52 @@ mla_status mla_prefill_attention(const mla_bf16* q, const uint16_t* k_nope, cons
                                  int32_t pairing, mla_bf16* out, float* lse, void* workspace,
                                  size_t* ws_bytes, hipStream_t stream);
 
+/* Rotate rotary keys into a shared rotated-key buffer [K2-query "Join query
+ * parts": the rotary key is rotated at its position; GLM-kv: one rotary key
+ * per token, shared by every head]: dst[b, t_off+t, :] = rot(k_pe[b, t, :],
+ * pos[b, t]) (pos NULL = t_off + t). Together with mla_kv_expand (t_off, V^T
+ * layout) this appends a chunk of tokens to the cache that
+ * mla_prefill_attention_cached reads.
+ * Args: k_pe device bf16 [B, T, Dr] (not rotated); cos/sin device fp32
+ *   [table_len, Dr/2]; pos device int32 [B, T] or NULL; dst device
+ *   [B, Tcap, Dr] of type kv_dtype (rows t_off..t_off+T-1 written).
+ *   B, T >= 0 (an empty call is a no-op); Dr even in [2, 256];
+ *   t_off + T <= Tcap.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED,
+ *   MLA_ERR_ROPE_TYPE, MLA_ERR_HIP. */
+mla_status mla_rotate_rope_key(const mla_bf16* k_pe, const float* cos, const float* sin, int32_t table_len,
+                               const int32_t* pos, int32_t B, int32_t T, int32_t Dr, int32_t pairing, uint16_t* dst,
+                               int32_t Tcap, int32_t t_off, int32_t kv_dtype, hipStream_t stream);
+
+/* Causal attention of a chunk of T new query tokens against a cache holding
+ * `past` earlier tokens and the chunk itself [K2-query "Join query parts":
+ * with past key values the cache is updated first and the causal mask is
+ * offset by the cached length]:
+ *   Q[b,h,t] = [ q[b,h,t,0:Dn] | rot(q[b,h,t,Dn:], pos[b,t]) ]  (pos NULL =
+ *              past + t)
+ *   K[b,h,s] = [ k_nope[b,h,s,:] | k_rot[b,s,:] ],  V[b,h,s] = V^T[b,h,:,s]
+ *   S[t,s] = scale * Q[t] . K[s] for s <= past + t (rows past+t+1.. masked),
+ *   P = softmax, out[b,h,t,:] = P V, lse as in mla_prefill_attention.
+ * With past = 0 and Tcap = T this is mla_prefill_attention on prepared
+ * operands. The cache rows 0..past+T-1 must already hold the chunk's keys
+ * and values (mla_kv_expand with t_off = past, mla_rotate_rope_key).
+ * Args: q device bf16 [B, H, T, Dn+Dr]; k_nope device [B, H, Tcap, Dn];
+ *   k_rot device [B, Tcap, Dr] (rotated); vt device V^T [B, H, Dv, v_ld],
+ *   v_ld >= past+T and a multiple of 8, columns past+T..v_ld-1 finite (a
+ *   cache allocated zeroed satisfies this); all of type kv_dtype; cos/sin
+ *   device fp32 [table_len, Dr/2]; out device bf16 [B, H, T, Dv]; lse device
+ *   fp32 [B, H, T] or NULL. past >= 0, past + T <= Tcap; supported (Dn+Dr,
+ *   Dv) as for mla_prefill_attention; one (b, h) slice of k_nope and of V^T
+ *   below 2 GiB. No workspace.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED,
+ *   MLA_ERR_ROPE_TYPE, MLA_ERR_HIP. */
+mla_status mla_prefill_attention_cached(const mla_bf16* q, const uint16_t* k_nope, const uint16_t* k_rot,
+                                        const uint16_t* vt, int32_t v_ld, int32_t kv_dtype, const float* cos,
+                                        const float* sin, int32_t table_len, const int32_t* pos, int32_t B,
+                                        int32_t H, int32_t T, int32_t past, int32_t Tcap, int32_t Dn, int32_t Dr,
+                                        int32_t Dv, float scale, int32_t pairing, mla_bf16* out, float* lse,
+                                        hipStream_t stream);
+
 /* Decode attention of one new token per sequence against an expanded cache
  * [K2-query: expanded cache update then scaled, masked softmax attention]:
  *   Q[b,h] = [ q[b,h,0,0:Dn] | rot(q[b,h,0,Dn:], q_pos[b]) ]

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared()
-    assert len(names) == 10
+    assert len(names) == 12
     assert sorted(_lib.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -231,3 +231,43 @@ def test_decode_absorbed_validation(lib):
     assert absorbed(lib, scale=0.0) == SHAPE
     assert absorbed(lib, table_len=0) == SHAPE
     assert absorbed(lib, cache=FAKE + 8) == SHAPE  # not 16-byte aligned
+
+
+def test_rotate_rope_key_validation(lib):
+    def call(kpe=FAKE, cos=FAKE, sin=FAKE, table_len=4096, pos=None, B=2, T=100, Dr=64, pairing=0, dst=FAKE,
+             Tcap=4096, t_off=0, dtype=1):
+        return lib.mla_rotate_rope_key(kpe, cos, sin, table_len, pos, B, T, Dr, pairing, dst, Tcap, t_off, dtype,
+                                       None)
+    assert call(T=0) == OK
+    assert call(T=0, kpe=None, dst=None) == OK
+    assert call(dst=None) == NULL
+    assert call(Dr=7) == SHAPE
+    assert call(t_off=4000) == SHAPE  # t_off + T > Tcap
+    assert call(t_off=-1) == SHAPE
+    assert call(table_len=50) == SHAPE  # positions t_off..t_off+T-1 need the table
+    assert call(dtype=7) == UNSUP
+    assert call(pairing=3) == ROPE
+
+
+def cached(lib, **kw):
+    a = dict(q=FAKE, kn=FAKE, kr=FAKE, vt=FAKE, v_ld=4096, dtype=1, cos=FAKE, sin=FAKE, table_len=4096, pos=None,
+             B=2, H=64, T=512, past=1024, Tcap=4096, Dn=128, Dr=64, Dv=128, scale=0.13, pairing=0, out=FAKE,
+             lse=None)
+    a.update(kw)
+    return lib.mla_prefill_attention_cached(*a.values(), None)
+
+
+def test_prefill_cached_validation(lib):
+    assert cached(lib, T=0) == OK
+    assert cached(lib, T=0, q=None) == OK
+    assert cached(lib, kr=None) == NULL
+    assert cached(lib, past=-1) == SHAPE
+    assert cached(lib, past=3700) == SHAPE  # past + T > Tcap
+    assert cached(lib, v_ld=1500) == SHAPE  # v_ld < past + T
+    assert cached(lib, v_ld=4092) == SHAPE  # not a multiple of 8
+    assert cached(lib, Dn=96) == UNSUP
+    assert cached(lib, dtype=4) == UNSUP
+    assert cached(lib, pairing=2) == ROPE
+    assert cached(lib, scale=-1.0) == SHAPE
+    assert cached(lib, table_len=1000) == SHAPE
+    assert cached(lib, vt=FAKE + 4) == SHAPE
