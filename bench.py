@@ -20,6 +20,8 @@ Reported (one JSON line):
                   against the MI355X dense 16-bit MFMA peak
   decode          decode attention GB/s (algorithmic bytes) and HBM fraction
   decode_latent   step time of the latent-cache decode and its attention
+  decode_latent_reexpand  the same latent-cache decode by re-expanding every
+                  cached row on each call (timed after the steps)
   chunked         prefill against a past cache: the last 1024-token chunk of
                   the 8k sequence attending to its 7168 cached rows (timed
                   after the steps, attention call only)
@@ -261,6 +263,25 @@ def main():
     torch.cuda.synchronize()
     t_chunk = mean([ce[i].elapsed_time(ce[i + 1]) for i in range(10)]) * 1e-3
     chunk_flops = 2.0 * wp.B * wp.H * (TQ * past + TQ * (TQ + 1) / 2) * (wp.Dqk + wp.Dv)
+
+    # latent-cache decode by re-expansion of every cached row (the eager
+    # alternative to the absorbed form), attention call only
+    tlat = mla.pipeline.build_table(rope_l, wl.cache_len, wl.Dqk, dev)
+    ws_rx = torch.empty((1400 << 20,), dtype=torch.uint8, device=dev)
+
+    def reexpand():
+        mla.api.mla_decode_latent_expanded(il["q"], il["W"], il["latent_cache"], seq_l, qpos_l, tlat.cos, tlat.sin,
+                                           tlat.scale, wl.Dn, wl.Dv, wl.pairing, 0, out=out_lat, workspace=ws_rx)
+    reexpand()
+    torch.cuda.synchronize()
+    re = [ev() for _ in range(6)]
+    re[0].record()
+    for i in range(5):
+        reexpand()
+        re[i + 1].record()
+    torch.cuda.synchronize()
+    t_rx = mean([re[i].elapsed_time(re[i + 1]) for i in range(5)]) * 1e-3
+    del ws_rx
     ms_step = wall * 1e3 / args.steps
     t_prefill = mean(rec["prefill"]) * 1e-3
     t_attn = mean(rec["attn"]) * 1e-3
@@ -277,7 +298,8 @@ def main():
         f"({attn_tflops:.1f} TFLOP/s, {attn_tflops / MFMA_PEAK_TFLOPS:.1%} of peak); decode step "
         f"{t_decode * 1e6:.1f} us, decode attention {t_dec_attn * 1e6:.1f} us ({dec_gbs:.0f} GB/s); latent-cache "
         f"decode step {t_lat * 1e6:.1f} us (attention {t_lat_attn * 1e6:.1f} us); chunked prefill (1024 after "
-        f"7168) {t_chunk * 1e3:.3f} ms ({chunk_flops / t_chunk / 1e12:.1f} TFLOP/s)")
+        f"7168) {t_chunk * 1e3:.3f} ms ({chunk_flops / t_chunk / 1e12:.1f} TFLOP/s); latent-cache decode by "
+        f"re-expansion {t_rx * 1e6:.0f} us")
 
     result = {
         "metric": "MLA prefill attn TFLOP/s + % bf16 MFMA peak; decode GB/s at 1k ctx",
@@ -314,6 +336,7 @@ def main():
             "decode_latent_tokens_per_s": round(wl.B / t_lat, 1),
             "decode_latent_cache_bytes": int(lat_bytes),
             "decode_latent_cache_gbs": round(lat_bytes / t_lat_attn / 1e9, 1),
+            "decode_latent_reexpand_attention_us": round(t_rx * 1e6, 1),
             "chunked_prefill_workload": f"{PREFILL} last {TQ} tokens after {past} cached rows",
             "chunked_prefill_attention_ms": round(t_chunk * 1e3, 4),
             "chunked_prefill_attention_tflops": round(chunk_flops / t_chunk / 1e12, 2),

@@ -32,7 +32,8 @@ V_ROWS, V_COLS = 0, 1
 EXPORTS = [
     "mla_rope_table_build", "mla_softmax_scale", "mla_latent_rmsnorm", "mla_kv_expand",
     "mla_prefill_attention", "mla_decode_attention", "mla_absorb_prepare", "mla_latent_cache_append",
-    "mla_decode_absorbed", "mla_rotate_rope_key", "mla_prefill_attention_cached", "mla_status_string",
+    "mla_decode_absorbed", "mla_rotate_rope_key", "mla_prefill_attention_cached", "mla_decode_latent_expanded",
+    "mla_status_string",
 ]
 
 
@@ -91,6 +92,8 @@ def load() -> ctypes.CDLL:
     lib.mla_rotate_rope_key.argtypes = [P, P, P, I32, P, I32, I32, I32, I32, P, I32, I32, I32, P]
     lib.mla_prefill_attention_cached.argtypes = [P, P, P, P, I32, I32, P, P, I32, P, I32, I32, I32, I32, I32, I32,
                                                  I32, I32, F32, I32, P, P, P]
+    lib.mla_decode_latent_expanded.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, F32, I32,
+                                               I32, P, SZ, P, P]
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]

@@ -19,7 +19,7 @@ __all__ = [
     "RopeParams", "rope_params", "mla_rope_table_build", "mla_softmax_scale", "mla_latent_rmsnorm",
     "mla_kv_expand", "mla_prefill_attention", "mla_decode_attention", "mla_absorb_prepare",
     "mla_latent_cache_append", "mla_decode_absorbed", "mla_rotate_rope_key", "mla_prefill_attention_cached",
-    "pairing_code",
+    "mla_decode_latent_expanded", "pairing_code",
     "PAIR_HALF", "PAIR_INTERLEAVED", "ROPE_DEFAULT", "ROPE_YARN",
 ]
 
@@ -439,4 +439,44 @@ def mla_decode_absorbed(q: torch.Tensor, W: torch.Tensor, w_ukt: torch.Tensor, c
     have = ctypes.c_size_t(workspace.numel())
     check("mla_decode_absorbed",
           lib.mla_decode_absorbed(*head, _ptr(workspace), ctypes.byref(have), _ptr(out), _stream(q)))
+    return out
+
+
+def mla_decode_latent_expanded(q: torch.Tensor, W: torch.Tensor, cache: torch.Tensor, seq_len: torch.Tensor,
+                               q_pos: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor, scale: float, Dn: int,
+                               Dv: int, pairing="half", num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The same output as mla_decode_absorbed, by re-expanding every cached
+    latent row into per-head keys and values on each call."""
+    _need(q, "q")
+    _need(W, "W")
+    _need(cache, "cache", torch.float16)
+    _need(seq_len, "seq_len", torch.int32)
+    _need(q_pos, "q_pos", torch.int32)
+    _need(cos, "cos", torch.float32)
+    _need(sin, "sin", torch.float32)
+    B, H, _, Dqk = q.shape
+    Dr = Dqk - Dn
+    Lcap, RW = cache.shape[1], cache.shape[2]
+    R = RW - Dr
+    _shape(W, "W", (H * (Dn + Dv), R))
+    _shape(cache, "cache", (B, Lcap, R + Dr))
+    _shape(seq_len, "seq_len", (B,))
+    _shape(q_pos, "q_pos", (B,))
+    _shape(sin, "sin", cos.shape)
+    if out is None:
+        out = torch.empty((B, H, 1, Dv), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out")
+    _shape(out, "out", (B, H, 1, Dv))
+    lib = _lib.load()
+    head = (_ptr(q), _ptr(W), _ptr(cache), _ptr(seq_len), _ptr(q_pos), _ptr(cos), _ptr(sin), cos.shape[0], B, H,
+            Lcap, R, Dn, Dr, Dv, float(scale), pairing_code(pairing), int(num_splits))
+    need = ctypes.c_size_t(0)
+    check("mla_decode_latent_expanded",
+          lib.mla_decode_latent_expanded(*head, None, ctypes.byref(need), _ptr(out), _stream(q)))
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty((need.value,), dtype=torch.uint8, device=q.device)
+    have = ctypes.c_size_t(workspace.numel())
+    check("mla_decode_latent_expanded",
+          lib.mla_decode_latent_expanded(*head, _ptr(workspace), ctypes.byref(have), _ptr(out), _stream(q)))
     return out

@@ -401,4 +401,56 @@ mla_status mla_decode_absorbed(const mla_bf16* q, const mla_bf16* W, const mla_b
   return hip_status(mla::launch_unabsorb(ua, stream));
 }
 
+mla_status mla_decode_latent_expanded(const mla_bf16* q, const mla_bf16* W, const uint16_t* cache,
+                                      const int32_t* seq_len, const int32_t* q_pos, const float* cos,
+                                      const float* sin, int32_t table_len, int32_t B, int32_t H, int32_t Lcap,
+                                      int32_t R, int32_t Dn, int32_t Dr, int32_t Dv, float scale, int32_t pairing,
+                                      int32_t num_splits, void* workspace, size_t* ws_bytes, mla_bf16* out,
+                                      hipStream_t stream) {
+  if (B < 0 || B > 65535 || H < 1 || H > 65535 || Lcap < 1) return MLA_ERR_SHAPE;
+  if (R < 8 || R > 4096 || (R % 8) || Dr < 8 || Dr > 256 || (Dr % 8)) return MLA_ERR_SHAPE;
+  if (!mla::decode_supported(Dn + Dr, Dv)) return MLA_ERR_UNSUPPORTED;
+  if (Dn < 8 || (Dn % 8) || Dv < 8 || (Dv % 8)) return MLA_ERR_SHAPE;
+  if (!pairing_ok(pairing)) return MLA_ERR_ROPE_TYPE;
+  if (num_splits < 0 || num_splits > 256 || num_splits > Lcap) return MLA_ERR_SHAPE;
+  if ((int64_t)B * H * Lcap * (Dn + Dr + Dv) > kMaxElems || (int64_t)B * Lcap > ((int64_t)1 << 30)) return MLA_ERR_SHAPE;
+  if ((int64_t)H * (Dn + Dv) > ((int64_t)1 << 30)) return MLA_ERR_SHAPE;
+  const int S = num_splits ? num_splits : mla::decode_auto_splits(B, H, Lcap);
+  const size_t c_bytes = round256((size_t)B * Lcap * R * 2);
+  const size_t k_bytes = round256((size_t)B * H * Lcap * (Dn + Dr) * 2);
+  const size_t v_bytes = round256((size_t)B * H * Lcap * Dv * 2);
+  const size_t need = c_bytes + k_bytes + v_bytes + mla::decode_workspace_bytes(B, H, Dv, S);
+  if (!workspace && ws_bytes) {
+    *ws_bytes = need;
+    return MLA_OK;
+  }
+  if (!(scale > 0.0f) || !isfinite(scale)) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!q || !W || !cache || !seq_len || !q_pos || !cos || !sin || !out) return MLA_ERR_NULL;
+  if (table_len < 1) return MLA_ERR_SHAPE;
+  if (!workspace || (ws_bytes && *ws_bytes < need)) return MLA_ERR_WORKSPACE;
+  if (!aligned16(W) || !aligned16(cache) || !aligned16(workspace)) return MLA_ERR_SHAPE;
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* c = reinterpret_cast<uint16_t*>(ws);
+  uint16_t* k = reinterpret_cast<uint16_t*>(ws + c_bytes);
+  uint16_t* v = reinterpret_cast<uint16_t*>(ws + c_bytes + k_bytes);
+  float* part_o = reinterpret_cast<float*>(ws + c_bytes + k_bytes + v_bytes);
+  float* part_ml = nullptr;
+  if (S > 1) {
+    const size_t n = (size_t)B * H * S;
+    part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(part_o) + round256(n * Dv * sizeof(float)));
+  }
+  clear_stale_error();
+  hipError_t e = mla::launch_latent_reexpand_copies(cache, c, k, B, H, Lcap, R, Dr, Dn, stream);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  // every cached latent row expanded into the per-head key (columns 0..Dn)
+  // and value caches: one prefill-size expansion per call
+  mla::ExpandArgs xa{c, W, k, v, B, Lcap, R, H, Dn, Dv, Dn + Dr, Lcap, 0, MLA_DTYPE_FP16, 0, 0};
+  e = mla::launch_kv_expand(xa, stream);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  mla::DecodeArgs da{q, k, v, seq_len, q_pos, cos, sin, table_len, B, H, Lcap, Dn, Dr, Dv, pairing, S,
+                     scale, part_o, part_ml, out, MLA_DTYPE_FP16};
+  return hip_status(mla::launch_decode(da, stream));
+}
+
 }  // extern "C"

@@ -236,6 +236,7 @@ bool decode_supported(int Dqk, int Dv) {
 int decode_auto_splits(int B, int H, int Tcap) {
   // aim at >= 2048 workgroups (8 per CU) without splits shorter than 256 keys
   const int bh = B * H;
+  if (bh <= 0) return 1;  // an empty batch: no launch follows
   int s = (2048 + bh - 1) / bh;
   const int smax = (Tcap + 255) / 256;
   if (s > smax) s = smax;

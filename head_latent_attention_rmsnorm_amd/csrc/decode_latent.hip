@@ -656,4 +656,51 @@ hipError_t launch_unabsorb(const UnabsorbArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Re-expansion of a latent cache (the GLM-5 page's eager form: every cached
+// latent is expanded by kv_b_proj on every call). The expansion itself is
+// kv_expand's tile kernel; these two copies adapt the cache rows to it and
+// to the expanded-cache decode kernel.
+
+// Latent part of each cache row -> contiguous [rows, R] (kv_expand's input).
+__global__ void __launch_bounds__(256) latent_gather_kernel(const uint16_t* __restrict__ cache,
+                                                            uint16_t* __restrict__ c, long rows, int R, int RW) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int n8 = R / 8;
+  if (idx >= rows * n8) return;
+  const long r = idx / n8;
+  const int e = (int)(idx % n8) * 8;
+  *reinterpret_cast<u32x4*>(c + r * R + e) = *reinterpret_cast<const u32x4*>(cache + r * RW + e);
+}
+
+// Rotated rotary key of cache row s of sequence b -> columns Dn..Dn+Dr of
+// row s of every head's key cache [B, H, Lcap, Dn+Dr] (the shared key
+// broadcast to all heads, GLM-5 expand_kv).
+__global__ void __launch_bounds__(256) rope_broadcast_kernel(const uint16_t* __restrict__ cache,
+                                                             uint16_t* __restrict__ k, int B, int H, int Lcap, int R,
+                                                             int Dr, int Dn) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int n8 = Dr / 8;
+  if (idx >= (long)B * Lcap * n8) return;
+  const long bs = idx / n8;
+  const int e = (int)(idx % n8) * 8;
+  const int b = (int)(bs / Lcap), s = (int)(bs % Lcap);
+  const u32x4 v = *reinterpret_cast<const u32x4*>(cache + bs * (R + Dr) + R + e);
+  const int Dqk = Dn + Dr;
+  for (int h = 0; h < H; ++h)
+    *reinterpret_cast<u32x4*>(k + (((size_t)b * H + h) * Lcap + s) * Dqk + Dn + e) = v;
+}
+
+hipError_t launch_latent_reexpand_copies(const uint16_t* cache, uint16_t* c, uint16_t* k, int B, int H, int Lcap,
+                                         int R, int Dr, int Dn, hipStream_t stream) {
+  const long rows = (long)B * Lcap;
+  const long n1 = rows * (R / 8);
+  hipLaunchKernelGGL(latent_gather_kernel, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, stream, cache, c, rows,
+                     R, R + Dr);
+  const long n2 = rows * (Dr / 8);
+  hipLaunchKernelGGL(rope_broadcast_kernel, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, stream, cache, k, B, H,
+                     Lcap, R, Dr, Dn);
+  return hipGetLastError();
+}
+
 }  // namespace mla

@@ -160,4 +160,10 @@ struct UnabsorbArgs {
 };
 hipError_t launch_unabsorb(const UnabsorbArgs& a, hipStream_t stream);
 
+// latent cache -> contiguous latent rows [B*Lcap, R] and the rotated key
+// broadcast into columns Dn.. of the expanded key cache [B, H, Lcap, Dn+Dr]
+// (R and Dr multiples of 8, rows 16-byte aligned)
+hipError_t launch_latent_reexpand_copies(const uint16_t* cache, uint16_t* c, uint16_t* k, int B, int H, int Lcap,
+                                         int R, int Dr, int Dn, hipStream_t stream);
+
 }  // namespace mla

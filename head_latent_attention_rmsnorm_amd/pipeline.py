@@ -82,15 +82,22 @@ def decode_step(q, latent, k_pe, gain, W, k_cache, v_cache, seq_len, q_pos, slot
 
 
 def decode_latent_step(q, latent, k_pe, gain, W, w_ukt, cache, seq_len, q_pos, table: RopeTable, Dn: int, Dv: int,
-                       pairing="half", eps: float = 1e-6, num_splits: int = 0, out=None, workspace=None):
+                       pairing="half", eps: float = 1e-6, num_splits: int = 0, out=None, workspace=None,
+                       method: str = "absorbed"):
     """One decode step against a latent cache [B, Lcap, R+Dr] fp16: the new
     token (q [B,H,1,Dqk], latent [B,1,R], k_pe [B,1,Dr]) is normalised and
     its rotary key rotated into cache row q_pos[b], then it attends over
-    seq_len[b] rows by the absorbed form. w_ukt comes from
-    api.mla_absorb_prepare(W, ...) (once per weight)."""
+    seq_len[b] rows, by the absorbed form (w_ukt from
+    api.mla_absorb_prepare, once per weight) or, with method="expand", by
+    re-expanding every cached row (w_ukt unused)."""
     B = latent.shape[0]
     api.mla_latent_cache_append(latent.view(B, -1), gain, k_pe.view(B, -1), table.cos, table.sin, q_pos, cache,
                                 eps, pairing)
+    if method == "expand":
+        return api.mla_decode_latent_expanded(q, W, cache, seq_len, q_pos, table.cos, table.sin, table.scale, Dn, Dv,
+                                              pairing, num_splits, out=out, workspace=workspace)
+    if method != "absorbed":
+        raise ValueError(f"method must be 'absorbed' or 'expand', not {method!r}")
     return api.mla_decode_absorbed(q, W, w_ukt, cache, seq_len, q_pos, table.cos, table.sin, table.scale, Dn, Dv,
                                    pairing, num_splits, out=out, workspace=workspace)
 

@@ -361,6 +361,30 @@ mla_status mla_decode_absorbed(const mla_bf16* q, const mla_bf16* W, const mla_b
                                int32_t Dr, int32_t Dv, float scale, int32_t pairing, int32_t num_splits,
                                void* workspace, size_t* ws_bytes, mla_bf16* out, hipStream_t stream);
 
+/* The same decode output against a latent cache by re-expansion [GLM-kv
+ * "KV cache": every cached latent and rotated key come back and the key and
+ * value heads are expanded from all of them on every call; expand_kv]:
+ * every cache row 0..Lcap-1 is expanded by kv_b_proj into per-head fp16 keys
+ * [W_uk[h] c_s | k_s] and values W_uv[h] c_s in the workspace, then the
+ * expanded-cache decode attention (split-K + combine) runs over rows
+ * s < seq_len[b]. Costs one prefill-size expansion of Lcap rows per call;
+ * mla_decode_absorbed computes the same output without it.
+ * Args: q device bf16 [B, H, 1, Dn+Dr]; W device bf16 [H*(Dn+Dv), R]; cache
+ *   device fp16 [B, Lcap, R+Dr]; seq_len device int32 [B] (clamped to
+ *   [1, Lcap]); q_pos device int32 [B]; cos/sin device fp32
+ *   [table_len, Dr/2]; num_splits 0 = automatic, else 1..256; out device
+ *   bf16 [B, H, 1, Dv]; workspace/ws_bytes as for mla_prefill_attention
+ *   (about B*H*Lcap*(Dn+Dr+Dv)*2 bytes). R and Dr multiples of 8 (R <= 4096,
+ *   Dr <= 256), (Dn+Dr, Dv) as for mla_decode_attention.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED,
+ *   MLA_ERR_ROPE_TYPE, MLA_ERR_WORKSPACE, MLA_ERR_HIP. */
+mla_status mla_decode_latent_expanded(const mla_bf16* q, const mla_bf16* W, const uint16_t* cache,
+                                      const int32_t* seq_len, const int32_t* q_pos, const float* cos,
+                                      const float* sin, int32_t table_len, int32_t B, int32_t H, int32_t Lcap,
+                                      int32_t R, int32_t Dn, int32_t Dr, int32_t Dv, float scale, int32_t pairing,
+                                      int32_t num_splits, void* workspace, size_t* ws_bytes, mla_bf16* out,
+                                      hipStream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* mla_status_string(mla_status s);
 

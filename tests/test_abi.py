@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared()
-    assert len(names) == 12
+    assert len(names) == 13
     assert sorted(_lib.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -166,6 +166,7 @@ def test_decode_validation(lib):
     assert decode(lib, ws=None) == WS
     assert decode(lib, dtype=3) == UNSUP
     assert decode(lib, B=0) == OK
+    assert decode(lib, B=0, splits=0) == OK  # automatic split count of an empty batch
 
 
 def test_absorb_prepare_validation(lib):
@@ -271,3 +272,25 @@ def test_prefill_cached_validation(lib):
     assert cached(lib, scale=-1.0) == SHAPE
     assert cached(lib, table_len=1000) == SHAPE
     assert cached(lib, vt=FAKE + 4) == SHAPE
+
+
+def reexpand(lib, ws=FAKE, ws_bytes=None, **kw):
+    a = dict(q=FAKE, W=FAKE, cache=FAKE, seq=FAKE, qpos=FAKE, cos=FAKE, sin=FAKE, table_len=1001, B=32, H=64,
+             Lcap=1001, R=512, Dn=128, Dr=64, Dv=128, scale=0.13, pairing=0, splits=0)
+    a.update(kw)
+    return lib.mla_decode_latent_expanded(*a.values(), ws, ws_bytes, FAKE, None)
+
+
+def test_decode_latent_expanded_validation(lib):
+    need = ctypes.c_size_t(0)
+    assert reexpand(lib, ws=None, ws_bytes=ctypes.byref(need)) == OK
+    assert need.value >= 32 * 64 * 1001 * (192 + 128) * 2  # the expanded keys and values
+    assert reexpand(lib, ws=None) == WS
+    assert reexpand(lib, B=0) == OK
+    assert reexpand(lib, cache=None) == NULL
+    assert reexpand(lib, Dn=96) == UNSUP
+    assert reexpand(lib, R=100) == SHAPE
+    assert reexpand(lib, Dr=12, Dn=180) == SHAPE
+    assert reexpand(lib, pairing=4) == ROPE
+    assert reexpand(lib, splits=300) == SHAPE
+    assert reexpand(lib, cache=FAKE + 8) == SHAPE

@@ -147,3 +147,43 @@ def test_decode_absorbed_kimi():
     for S in (1, 5, 16):
         d = np.abs(f64(outs[S]) - f64(outs[0]))
         assert np.all(d <= np.abs(f64(outs[0])) * 2.0 ** -7 + 2e-3), (S, d.max())
+
+
+# ---- the same outputs by re-expanding the latent cache on every call
+
+def run_expand(w, inp, q_pos, num_splits=0):
+    g = {k: v.cuda() for k, v in inp.items()}
+    qp = torch.tensor(q_pos, dtype=torch.int32, device="cuda")
+    tab = table(w, w.cache_len)
+    cache = g["latent_cache"].clone()
+    out = pipeline.decode_latent_step(g["q"], g["latent"], g["k_pe"], g["gain"], g["W"], None, cache, qp + 1, qp, tab,
+                                      w.Dn, w.Dv, w.pairing, w.eps, num_splits, method="expand")
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+@pytest.mark.parametrize("q_pos", [[36, 36, 36], [36, 0, 20]], ids=["uniform", "ragged"])
+def test_decode_latent_expanded_tiny(q_pos):
+    w = workloads.WORKLOADS["tiny_decode_latent"]
+    inp = workloads.make_inputs(w)
+    ref = O.decode_latent(w, inp, q_pos=q_pos)
+    for S in (0, 1, 2):
+        say(f"[latent expand] tiny q_pos={q_pos} splits={S}")
+        assert_close(f64(run_expand(w, inp, q_pos, S)), ref, f"re-expansion tiny splits={S}")
+
+
+def test_decode_latent_expanded_kimi_agrees_with_absorbed():
+    w = workloads.WORKLOADS["kimi_k2_decode_latent"]
+    say("[latent expand] kimi_k2_decode_latent B=32 L=1001")
+    inp = workloads.make_inputs(w)
+    q_pos = [w.q_pos] * w.B
+    picks = [0, 31]
+    ref = O.decode_latent(w, inp, b_idx=picks)
+    out = run_expand(w, inp, q_pos)
+    ma, rl = errors(f64(out[picks]), ref)
+    say(f"  re-expansion: max-abs {ma:.3e} rel-L2 {rl:.3e}")
+    assert ma <= MAX_ABS and rl <= REL_L2
+    absorbed, _ = run(w, inp, q_pos)
+    ma, rl = errors(f64(out), f64(absorbed))  # every sequence: the two evaluations agree
+    say(f"  re-expansion vs absorbed, all sequences: max-abs {ma:.3e} rel-L2 {rl:.3e}")
+    assert ma <= MAX_ABS and rl <= REL_L2
