@@ -27,13 +27,14 @@ ROPE_DEFAULT, ROPE_YARN = 0, 1
 PAIR_HALF, PAIR_INTERLEAVED = 0, 1
 DTYPE_BF16, DTYPE_FP16 = 0, 1
 V_ROWS, V_COLS = 0, 1
+LIN_ROWS, LIN_HEADS, LIN_SPLIT = 0, 1, 2
 
 # every symbol the header declares
 EXPORTS = [
     "mla_rope_table_build", "mla_softmax_scale", "mla_latent_rmsnorm", "mla_kv_expand",
     "mla_prefill_attention", "mla_decode_attention", "mla_absorb_prepare", "mla_latent_cache_append",
     "mla_decode_absorbed", "mla_rotate_rope_key", "mla_prefill_attention_cached", "mla_decode_latent_expanded",
-    "mla_status_string",
+    "mla_linear", "mla_status_string",
 ]
 
 
@@ -94,6 +95,7 @@ def load() -> ctypes.CDLL:
                                                  I32, I32, F32, I32, P, P, P]
     lib.mla_decode_latent_expanded.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, F32, I32,
                                                I32, P, SZ, P, P]
+    lib.mla_linear.argtypes = [P, I32, I32, I32, P, P, I32, I32, I32, P, P, I32, I32, I32, I32, P]
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]

@@ -19,7 +19,7 @@ __all__ = [
     "RopeParams", "rope_params", "mla_rope_table_build", "mla_softmax_scale", "mla_latent_rmsnorm",
     "mla_kv_expand", "mla_prefill_attention", "mla_decode_attention", "mla_absorb_prepare",
     "mla_latent_cache_append", "mla_decode_absorbed", "mla_rotate_rope_key", "mla_prefill_attention_cached",
-    "mla_decode_latent_expanded", "pairing_code",
+    "mla_decode_latent_expanded", "mla_linear", "pairing_code",
     "PAIR_HALF", "PAIR_INTERLEAVED", "ROPE_DEFAULT", "ROPE_YARN",
 ]
 
@@ -480,3 +480,60 @@ def mla_decode_latent_expanded(q: torch.Tensor, W: torch.Tensor, cache: torch.Te
     check("mla_decode_latent_expanded",
           lib.mla_decode_latent_expanded(*head, _ptr(workspace), ctypes.byref(have), _ptr(out), _stream(q)))
     return out
+
+
+def mla_linear(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None, x_heads: bool = False,
+               out_heads: Optional[Tuple[int, int]] = None, split: Optional[int] = None,
+               out: Optional[torch.Tensor] = None):
+    """Y = X W^T (+ bias) in bf16 with fp32 accumulation. w [N, K].
+
+    X: [M, K], or with x_heads=True the head-major [B, Hx, T, Dx] tensor read
+    as [B*T, Hx*Dx]. Y: [M, N] (for a head-major X: [B, T, N]); with
+    out_heads=(H, D) the head-major [B, H, T, D] (N = H*D; B, T from X's
+    leading dimensions); with split=s the pair ([..., s], [..., N-s])."""
+    _need(x, "x")
+    _need(w, "w")
+    N, K = w.shape
+    if x_heads:
+        if x.dim() != 4:
+            raise ValueError(f"a head-major x should be [B, H, T, D], but is {tuple(x.shape)}")
+        B, Hx, T, Dx = x.shape
+        if Hx * Dx != K:
+            raise ValueError(f"x heads {Hx} x {Dx} do not match w's K = {K}")
+        M, lead, xl, xT, xD = B * T, (B, T), _lib.LIN_HEADS, T, Dx
+    else:
+        if x.shape[-1] != K:
+            raise ValueError(f"x's last dimension {x.shape[-1]} does not match w's K = {K}")
+        lead = tuple(x.shape[:-1])
+        M = int(torch.tensor(lead).prod()) if lead else 1
+        xl, xT, xD = _lib.LIN_ROWS, 0, 0
+        B = lead[0] if len(lead) >= 2 else 1
+        T = M // B
+    if bias is not None:
+        _need(bias, "bias")
+        _shape(bias, "bias", (N,))
+    y1 = None
+    yT = yD = ys = 0
+    if out_heads is not None:
+        Hy, Dy = out_heads
+        if Hy * Dy != N:
+            raise ValueError(f"out_heads {out_heads} do not match N = {N}")
+        yl, yT, yD = _lib.LIN_HEADS, (lead[-1] if len(lead) >= 2 else M), Dy
+        Bo = M // yT
+        if out is None:
+            out = torch.empty((Bo, Hy, yT, Dy), dtype=torch.bfloat16, device=x.device)
+        _shape(out, "out", (Bo, Hy, yT, Dy))
+    elif split is not None:
+        yl, ys = _lib.LIN_SPLIT, int(split)
+        y0 = torch.empty(lead + (ys,), dtype=torch.bfloat16, device=x.device)
+        y1 = torch.empty(lead + (N - ys,), dtype=torch.bfloat16, device=x.device)
+        out = y0
+    else:
+        yl = _lib.LIN_ROWS
+        if out is None:
+            out = torch.empty(lead + (N,), dtype=torch.bfloat16, device=x.device)
+        _shape(out, "out", lead + (N,))
+    _need(out, "out")
+    check("mla_linear", _lib.load().mla_linear(_ptr(x), xl, xT, xD, _ptr(w), _ptr(bias), M, N, K, _ptr(out),
+                                               _ptr(y1), yl, yT, yD, ys, _stream(x)))
+    return (out, y1) if split is not None else out

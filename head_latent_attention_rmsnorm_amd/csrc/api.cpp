@@ -453,4 +453,36 @@ mla_status mla_decode_latent_expanded(const mla_bf16* q, const mla_bf16* W, cons
   return hip_status(mla::launch_decode(da, stream));
 }
 
+mla_status mla_linear(const mla_bf16* x, int32_t x_layout, int32_t x_T, int32_t x_D, const mla_bf16* w,
+                      const mla_bf16* bias, int32_t M, int32_t N, int32_t K, mla_bf16* y0, mla_bf16* y1,
+                      int32_t y_layout, int32_t y_T, int32_t y_D, int32_t y_split, hipStream_t stream) {
+  if (M < 0 || N < 8 || (N % 8) || K < 64 || (K % 64)) return MLA_ERR_SHAPE;
+  // byte offsets into X, W and Y are 32-bit
+  if ((int64_t)M * K >= ((int64_t)1 << 31) || (int64_t)N * K >= ((int64_t)1 << 31) ||
+      (int64_t)M * N >= ((int64_t)1 << 31))
+    return MLA_ERR_SHAPE;
+  int dlog2 = 0;
+  if (x_layout == MLA_LIN_HEADS) {
+    if (x_D < 8 || x_D > 4096 || (x_D & (x_D - 1)) || (K % x_D) || x_T < 1 || (M % x_T)) return MLA_ERR_SHAPE;
+    while ((1 << dlog2) < x_D) ++dlog2;
+  } else if (x_layout != MLA_LIN_ROWS) {
+    return MLA_ERR_SHAPE;
+  }
+  if (y_layout == MLA_LIN_HEADS) {
+    if (y_D < 8 || (y_D % 8) || (N % y_D) || y_T < 1 || (M % y_T)) return MLA_ERR_SHAPE;
+  } else if (y_layout == MLA_LIN_SPLIT) {
+    if (y_split < 8 || y_split >= N || (y_split % 8)) return MLA_ERR_SHAPE;
+  } else if (y_layout != MLA_LIN_ROWS) {
+    return MLA_ERR_SHAPE;
+  }
+  if (M == 0) return MLA_OK;
+  if (!x || !w || !y0 || (y_layout == MLA_LIN_SPLIT && !y1)) return MLA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y0) || (y1 && !aligned16(y1))) return MLA_ERR_SHAPE;
+  if (bias && (((uintptr_t)bias) & 7)) return MLA_ERR_SHAPE;
+  clear_stale_error();
+  mla::LinearArgs a{x, w, bias, y0, y1, M, N, K, x_layout == MLA_LIN_HEADS ? 1 : 0, x_T, dlog2, y_layout, y_T, y_D,
+                    y_split};
+  return hip_status(mla::launch_linear(a, stream));
+}
+
 }  // extern "C"

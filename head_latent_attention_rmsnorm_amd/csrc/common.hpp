@@ -115,4 +115,32 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t b
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
 }
 
+// LDS operand images for 16-bit MFMA operands loaded by 16-byte LDS-direct
+// loads (lane i of a load writes bytes 16i..16i+15 of a 1 KB block).
+// A group of SW 1 KB blocks (SW = 1, 2 or 4) holds SW 16-deep k-steps of the
+// 32 rows one 32x32 MFMA operand covers. Row r (0..31) lives in block
+// r / (32/SW) of the group at byte (r % (32/SW)) * 32*SW (32*SW contiguous
+// bytes of the row: with SW = 4 one load instruction brings 8 whole
+// 128-byte row segments); its 16-byte chunk x (0..2SW-1) sits at chunk
+// position x ^ swz(r). With 16 lanes per LDS cycle (rows r..r+15 of one
+// k-step, same chunk), the pairs (row position mod 256 bytes, chunk
+// position) are all distinct, so the 16 reads hit 16 different 4-bank groups.
+template <int SW>
+__device__ __forceinline__ int frag_swz(int r) {
+  return (r >> (SW == 4 ? 1 : SW == 2 ? 2 : 3)) & (2 * SW - 1);
+}
+// Byte offset in the group of the chunk that lane (row r, half g) reads for
+// k-step 0; k-step c is at this offset XOR 32c.
+template <int SW>
+__device__ __forceinline__ int frag_read0(int r, int g) {
+  constexpr int RL = 32 / SW;
+  return (r / RL) * 1024 + (r % RL) * (32 * SW) + ((frag_swz<SW>(r) ^ g) << 4);
+}
+// Row r and chunk x that load lane i writes into block rb of a group.
+template <int SW>
+__device__ __forceinline__ void frag_slot(int rb, int i, int& r, int& x) {
+  r = rb * (32 / SW) + i / (2 * SW);
+  x = (i % (2 * SW)) ^ frag_swz<SW>(r);
+}
+
 }  // namespace mla

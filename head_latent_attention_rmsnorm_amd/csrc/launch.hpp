@@ -166,4 +166,17 @@ hipError_t launch_unabsorb(const UnabsorbArgs& a, hipStream_t stream);
 hipError_t launch_latent_reexpand_copies(const uint16_t* cache, uint16_t* c, uint16_t* k, int B, int H, int Lcap,
                                          int R, int Dr, int Dn, hipStream_t stream);
 
+// ---- linear layer Y = X W^T (+ bias), bf16
+struct LinearArgs {
+  const uint16_t* x;     // x_mode 0: [M, K]; 1: [B, K/Dx, xT, Dx] with M = B*xT
+  const uint16_t* w;     // [N, K]
+  const uint16_t* bias;  // [N] or null
+  uint16_t* y0;          // y_mode 0: [M, N]; 1: [B, N/yD, yT, yD]; 2: [M, ys]
+  uint16_t* y1;          // y_mode 2: [M, N - ys]
+  int M, N, K;
+  int x_mode, xT, x_dlog2;
+  int y_mode, yT, yD, ys;
+};
+hipError_t launch_linear(const LinearArgs& a, hipStream_t stream);
+
 }  // namespace mla

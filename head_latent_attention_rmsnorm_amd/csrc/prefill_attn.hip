@@ -79,29 +79,6 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, 0, 0, 0);
 }
 
-// Operand groups of SW 1 KB blocks (SW = 1, 2 or 4 k-steps of 16 elements
-// for 32 operand rows). Row r (0..31) lives in block r / (32/SW) of the
-// group at byte (r % (32/SW)) * 32*SW; its 16-byte chunk x (0..2SW-1) sits
-// at chunk position x ^ swz(r). With 16 lanes per LDS cycle (rows r..r+15
-// of one k-step, same chunk), the pairs (row position mod 256 bytes, chunk
-// position) are all distinct, so the 16 reads hit 16 different 4-bank groups.
-template <int SW>
-__device__ __forceinline__ int frag_swz(int r) {
-  return (r >> (SW == 4 ? 1 : SW == 2 ? 2 : 3)) & (2 * SW - 1);
-}
-// Byte offset in the group of the chunk that lane (row r, half g) reads for
-// k-step 0; k-step c is at this offset XOR 32c.
-template <int SW>
-__device__ __forceinline__ int frag_read0(int r, int g) {
-  constexpr int RL = 32 / SW;
-  return (r / RL) * 1024 + (r % RL) * (32 * SW) + ((frag_swz<SW>(r) ^ g) << 4);
-}
-// Row r and chunk x that load lane i writes into block rb of a group.
-template <int SW>
-__device__ __forceinline__ void frag_slot(int rb, int i, int& r, int& x) {
-  r = rb * (32 / SW) + i / (2 * SW);
-  x = (i % (2 * SW)) ^ frag_swz<SW>(r);
-}
 }  // namespace
 
 template <class ET, int DQK, int DR, int DV, int BN, int NW, int MINW>

@@ -93,6 +93,7 @@ typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP16 = 1 } mla_dtype;
  * so it reads V^T directly; given ROWS it first transposes into its
  * workspace. */
 typedef enum { MLA_V_ROWS = 0, MLA_V_COLS = 1 } mla_v_layout;
+typedef enum { MLA_LIN_ROWS = 0, MLA_LIN_HEADS = 1, MLA_LIN_SPLIT = 2 } mla_linear_layout;
 
 /* Rotary parameters [K2-rope, YaRN class and rope_scaling keys]. The YaRN
  * class defaults printed on the page are base 10000, factor 1.0,
@@ -384,6 +385,30 @@ mla_status mla_decode_latent_expanded(const mla_bf16* q, const mla_bf16* W, cons
                                       int32_t R, int32_t Dn, int32_t Dr, int32_t Dv, float scale, int32_t pairing,
                                       int32_t num_splits, void* workspace, size_t* ws_bytes, mla_bf16* out,
                                       hipStream_t stream);
+
+/* ---- Projections around the latent attention ----------------------------
+ * Linear layer Y = X W^T (+ bias) [K2-query "Split content heads" and the
+ * MLA constructor: q_a_proj, q_b_proj, kv_a_proj_with_mqa and o_proj are
+ * nn.Linear layers (weight [out, in]); GLM-kv "Key-value compression": the
+ * same layers], bf16 operands, fp32 accumulation, one bf16 rounding (after
+ * the bias).
+ * Layouts (mla_linear_layout):
+ *   X: MLA_LIN_ROWS [M, K], or MLA_LIN_HEADS [B, K/x_D, x_T, x_D] read as
+ *      the [M = B*x_T, K] matrix whose row (b, t) is head 0..K/x_D-1 of
+ *      token t concatenated (the attention output feeding o_proj);
+ *   Y: MLA_LIN_ROWS [M, N]; MLA_LIN_HEADS [B, N/y_D, y_T, y_D] (column n of
+ *      row (b, t) goes to head n / y_D, element n % y_D: the query layout
+ *      q_b_proj feeds to the attention); MLA_LIN_SPLIT y0 [M, y_split] and
+ *      y1 [M, N - y_split] (kv_a_proj_with_mqa's latent and rotary key).
+ * Args: x, w device bf16 (w [N, K]); bias device bf16 [N] or NULL; y0/y1
+ *   device bf16 as above (y1 only for SPLIT). M >= 0 (0 is a no-op);
+ *   N a multiple of 8; K a multiple of 64; M*K, N*K, M*N < 2^31; x_D a
+ *   power of two in [8, 4096] dividing K; y_D and y_split multiples of 8;
+ *   x_T, y_T dividing M; x, w, y0, y1 16-byte aligned, bias 8-byte aligned.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_HIP. */
+mla_status mla_linear(const mla_bf16* x, int32_t x_layout, int32_t x_T, int32_t x_D, const mla_bf16* w,
+                      const mla_bf16* bias, int32_t M, int32_t N, int32_t K, mla_bf16* y0, mla_bf16* y1,
+                      int32_t y_layout, int32_t y_T, int32_t y_D, int32_t y_split, hipStream_t stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* mla_status_string(mla_status s);

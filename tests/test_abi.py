@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared()
-    assert len(names) == 13
+    assert len(names) == 14
     assert sorted(_lib.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -294,3 +294,30 @@ def test_decode_latent_expanded_validation(lib):
     assert reexpand(lib, pairing=4) == ROPE
     assert reexpand(lib, splits=300) == SHAPE
     assert reexpand(lib, cache=FAKE + 8) == SHAPE
+
+
+def linear(lib, **kw):
+    a = dict(x=FAKE, xl=0, xT=0, xD=0, w=FAKE, bias=None, M=1024, N=1536, K=7168, y0=FAKE, y1=None, yl=0, yT=0, yD=0,
+             ys=0)
+    a.update(kw)
+    return lib.mla_linear(*a.values(), None)
+
+
+def test_linear_validation(lib):
+    assert linear(lib, M=0) == OK
+    assert linear(lib, M=0, x=None) == OK
+    assert linear(lib, x=None) == NULL
+    assert linear(lib, y0=None) == NULL
+    assert linear(lib, yl=2, ys=512, N=576) == NULL  # split needs y1
+    assert linear(lib, K=100) == SHAPE  # K not a multiple of 64
+    assert linear(lib, N=100) == SHAPE  # N not a multiple of 8
+    assert linear(lib, M=-1) == SHAPE
+    assert linear(lib, xl=1, xT=1000, xD=128, K=8192) == SHAPE  # x_T does not divide M
+    assert linear(lib, xl=1, xT=512, xD=96, K=7680) == SHAPE  # x_D not a power of two
+    assert linear(lib, yl=1, yT=1024, yD=100, N=1500) == SHAPE  # y_D not a multiple of 8
+    assert linear(lib, yl=2, ys=516, N=576, y1=FAKE) == SHAPE
+    assert linear(lib, yl=3) == SHAPE
+    assert linear(lib, xl=2) == SHAPE
+    assert linear(lib, M=300000, K=8192) == SHAPE  # M*K >= 2^31
+    assert linear(lib, x=FAKE + 8) == SHAPE
+    assert linear(lib, bias=FAKE + 2) == SHAPE
