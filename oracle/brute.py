@@ -15,7 +15,10 @@ import math
 
 
 def _flat(t):
-    """bf16/fp32 torch tensor -> nested Python lists of floats (exact)."""
+    """bf16/fp32 torch tensor -> nested Python lists of floats (exact); nested
+    lists pass through unchanged."""
+    if isinstance(t, list):
+        return t
     return t.detach().float().tolist()
 
 
@@ -187,5 +190,41 @@ def decode_latent(w, inp, q_pos=None):
             vals = [expanded[s][1][h] for s in range(p + 1)]
             qrow = q[b][h][0][:w.Dn] + rot(q[b][h][0][w.Dn:], p, freqs, m, w.pairing)
             ob.append([_attend(qrow, keys, vals, scale)])
+        out.append(ob)
+    return out
+
+
+def _matvec(row, Wl):
+    """[sum_k row[k] * Wl[n][k] for each n] (nn.Linear on one row)."""
+    return [sum(row[k] * wn[k] for k in range(len(row))) for wn in Wl]
+
+
+def block_forward(w, inp):
+    """out[b][t][j] for a tiny block workload, by scalar loops: the
+    projections of every token, then `prefill` on them, then o_proj."""
+    h = _flat(inp["hidden"])
+    Wqa, gq, Wqb = _flat(inp["W_qa"]), _flat(inp["gain_q"]), _flat(inp["W_qb"])
+    Wkva, Wo = _flat(inp["W_kva"]), _flat(inp["W_o"])
+    q = [[[None] * w.T for _ in range(w.H)] for _ in range(w.B)]
+    lat, kpe = [], []
+    for b in range(w.B):
+        lb, kb = [], []
+        for t in range(w.T):
+            qa = _norm_row(_matvec(h[b][t], Wqa), gq, w.eps)
+            qt = _matvec(qa, Wqb)
+            for hh in range(w.H):
+                q[b][hh][t] = qt[hh * w.Dqk:(hh + 1) * w.Dqk]
+            kv = _matvec(h[b][t], Wkva)
+            lb.append(kv[:w.R])
+            kb.append(kv[w.R:])
+        lat.append(lb)
+        kpe.append(kb)
+    O = prefill(w, {"q": q, "latent": lat, "k_pe": kpe, "gain": _flat(inp["gain"]), "W": _flat(inp["W"])})
+    out = []
+    for b in range(w.B):
+        ob = []
+        for t in range(w.T):
+            x = [O[b][hh][t][j] for hh in range(w.H) for j in range(w.Dv)]
+            ob.append(_matvec(x, Wo))
         out.append(ob)
     return out

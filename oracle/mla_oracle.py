@@ -416,3 +416,36 @@ def decode_latent_absorbed(w, inp: dict, b_idx=None, q_pos=None) -> np.ndarray:
             P = e / e.sum()
             O[i, h] = (P @ rows[:, :w.R]) @ W_uv[h].T
     return O
+
+
+# ---------------------------------------------------------------------------
+# The whole attention block around the path [K2-query], [GLM-kv]
+# ---------------------------------------------------------------------------
+
+
+def block_inputs(w, inp: dict) -> dict:
+    """The path's inputs from the block's hidden states: q =
+    q_b_proj(q_a_layernorm(q_a_proj(h))) viewed [B, H, T, Dqk]; latent and
+    shared rotary key = the two parts of kv_a_proj_with_mqa(h) [K2-query,
+    "Split content heads" and the MLA constructor; GLM-kv, "Key-value
+    compression"]. nn.Linear: y = x W^T; no biases."""
+    h = _f64(inp["hidden"])
+    kva = h @ _f64(inp["W_kva"]).T
+    qa = rmsnorm(h @ _f64(inp["W_qa"]).T, _f64(inp["gain_q"]), w.eps)
+    q = (qa @ _f64(inp["W_qb"]).T).reshape(w.B, w.T, w.H, w.Dqk).transpose(0, 2, 1, 3)
+    return {"q": q, "latent": kva[..., :w.R], "k_pe": kva[..., w.R:], "gain": _f64(inp["gain"]),
+            "W": _f64(inp["W"])}
+
+
+def block_forward(w, inp: dict, rows=None) -> np.ndarray:
+    """Block output [B, len(rows), hidden] (default all rows): the eager
+    path on `block_inputs`, then o_proj on the heads' outputs concatenated
+    per token (attn_output transposed to [B, T, H*Dv], then y = x W_o^T)."""
+    parts = prefill_parts(w, block_inputs(w, inp))
+    rows = np.arange(w.T) if rows is None else np.asarray(rows)
+    O = np.empty((w.B, w.H, len(rows), w.Dv))
+    for b in range(w.B):
+        for h in range(w.H):
+            O[b, h] = prefill_head(w, parts, b, h, rows=rows)
+    x = O.transpose(0, 2, 1, 3).reshape(w.B, len(rows), w.H * w.Dv)
+    return x @ _f64(inp["W_o"]).T

@@ -276,3 +276,26 @@ def test_decode_latent_equals_prefill_last_row():
             "gain": inp["gain"], "W": inp["W"], "latent_cache": torch.from_numpy(cache)}
     out = O.decode_latent(wd, dinp)
     np.testing.assert_allclose(out[:, :, 0], ref[:, :, T - 1], rtol=1e-12, atol=1e-13)
+
+
+# ---- the whole attention block (projections around the path)
+
+def test_block_matches_brute_force():
+    w = dataclasses.replace(workloads.WORKLOADS["tiny_block"], T=9, B=2)
+    inp = workloads.make_inputs(w)
+    assert inp["hidden"].dtype == torch.bfloat16 and "q" not in inp
+    np.testing.assert_allclose(O.block_forward(w, inp), np.array(brute.block_forward(w, inp)), rtol=1e-10,
+                               atol=1e-12)
+
+
+def test_block_rows_and_inputs():
+    w = workloads.WORKLOADS["tiny_block"]
+    inp = workloads.make_inputs(w)
+    full = O.block_forward(w, inp)
+    assert full.shape == (w.B, w.T, w.hidden)
+    rows = [0, 7, 39]
+    np.testing.assert_allclose(O.block_forward(w, inp, rows=rows), full[:, rows], rtol=1e-13, atol=1e-14)
+    # the path's inputs come out at the scales the other workloads draw
+    bi = O.block_inputs(w, inp)
+    assert bi["q"].shape == (w.B, w.H, w.T, w.Dqk) and bi["latent"].shape == (w.B, w.T, w.R)
+    assert 0.5 < np.std(bi["q"]) < 2.0 and 0.5 < np.std(bi["latent"]) < 2.0

@@ -15,6 +15,14 @@ compressed latent and the single rotary key shared by all heads (first page,
 compression"), the latent RMSNorm gain and the kv_b_proj weight stored as an
 nn.Linear weight of shape [H*(Dn+Dv), R].
 
+Two block workloads start one step earlier, at the hidden states of the
+attention block: the query comes from the low-rank query projections with
+their RMSNorm, the latent and the shared rotary key from the joint
+key-value down-projection, and an output projection follows (Kimi-K2
+"Query content heads", the MLA constructor). The hidden size and query rank
+are not on the pages; the Kimi-K2 one uses Kimi-K2's published 7168 and
+1536, the tiny one 128 and 64; no projection has a bias.
+
 Two further decode workloads (a tiny one and a Kimi-K2-shape one) keep a
 compressed-latent cache instead of the expanded one: per token the
 normalised latent followed by the rotated shared rotary key (GLM-5
@@ -72,6 +80,8 @@ class Workload:
     cache_len: int = 0  # decode: number of cached rows including the new one
     q_pos: int = 0  # decode: position of the new token
     latent_cache: bool = False  # decode: the cache holds latents, not expanded keys/values
+    hidden: int = 0  # whole MLA block: hidden size (0: the inputs start at q / latent / k_pe)
+    q_lora: int = 0  # whole MLA block: rank of the query down-projection
 
     @property
     def Dqk(self) -> int:
@@ -104,6 +114,10 @@ WORKLOADS = {
     "kimi_k2_decode_latent": Workload("kimi_k2_decode_latent", B=32, T=1, H=64, R=512, Dn=128, Dr=64, Dv=128,
                                       rope=YARN_KIMI, pairing="half", seed=5, decode=True,
                                       cache_len=1001, q_pos=1000, latent_cache=True),
+    "tiny_block": Workload("tiny_block", B=2, T=40, H=4, R=64, Dn=32, Dr=16, Dv=32,
+                           rope=RopeSpec(kind="default", base=10000.0), pairing="half", seed=8, hidden=128, q_lora=64),
+    "kimi_k2_block_1k": Workload("kimi_k2_block_1k", B=1, T=1024, H=64, R=512, Dn=128, Dr=64, Dv=128,
+                                 rope=YARN_KIMI, pairing="half", seed=9, hidden=7168, q_lora=1536),
 }
 
 ORDER = ["tiny", "kimi_k2_1k", "kimi_k2_8k", "glm5_4k", "kimi_k2_decode"]
@@ -150,6 +164,19 @@ def make_inputs(w: Workload, with_cache: bool = True, device: str = "cpu") -> di
     """
     gen = torch.Generator(device=device)
     gen.manual_seed(w.seed)
+    if w.hidden:
+        # block workload: hidden states and the five projection weights
+        # (nn.Linear layout, std 1/sqrt(fan_in)) with the two RMSNorm gains
+        return {
+            "hidden": _normal(gen, (w.B, w.T, w.hidden)),
+            "W_qa": _normal(gen, (w.q_lora, w.hidden), std=1.0 / math.sqrt(w.hidden)),
+            "gain_q": _normal(gen, (w.q_lora,), std=math.sqrt(0.1), mean=1.0),
+            "W_qb": _normal(gen, (w.H * w.Dqk, w.q_lora), std=1.0 / math.sqrt(w.q_lora)),
+            "W_kva": _normal(gen, (w.R + w.Dr, w.hidden), std=1.0 / math.sqrt(w.hidden)),
+            "gain": _normal(gen, (w.R,), std=math.sqrt(0.1), mean=1.0),
+            "W": _normal(gen, (w.H * (w.Dn + w.Dv), w.R), std=1.0 / math.sqrt(w.R)),
+            "W_o": _normal(gen, (w.hidden, w.H * w.Dv), std=1.0 / math.sqrt(w.H * w.Dv)),
+        }
     out = {
         "q": _normal(gen, (w.B, w.H, w.T, w.Dqk)),
         "latent": _normal(gen, (w.B, w.T, w.R)),
