@@ -22,6 +22,9 @@ Reported (one JSON line):
   decode_latent   step time of the latent-cache decode and its attention
   decode_latent_reexpand  the same latent-cache decode by re-expanding every
                   cached row on each call (timed after the steps)
+  block           the whole attention block at the 8k prefill shape (hidden
+                  7168, q rank 1536): projections, query RMSNorm, the path,
+                  o_proj (timed after the steps)
   chunked         prefill against a past cache: the last 1024-token chunk of
                   the 8k sequence attending to its 7168 cached rows (timed
                   after the steps, attention call only)
@@ -282,6 +285,29 @@ def main():
     torch.cuda.synchronize()
     t_rx = mean([re[i].elapsed_time(re[i + 1]) for i in range(5)]) * 1e-3
     del ws_rx
+
+    # the whole attention block at the 8k prefill shape
+    import dataclasses
+    wb = dataclasses.replace(workloads.WORKLOADS["kimi_k2_block_1k"], B=wp.B, T=wp.T)
+    ib = workloads.make_inputs(wb, device=dev)
+    tb = mla.pipeline.build_table(mla.api.params_from(wb.rope, wb.Dr), wb.T, wb.Dqk, dev)
+
+    def block():
+        return mla.pipeline.block_forward(ib["hidden"], ib["W_qa"], ib["gain_q"], ib["W_qb"], ib["W_kva"], ib["gain"],
+                                          ib["W"], ib["W_o"], tb, wb.H, wb.Dn, wb.Dr, wb.Dv, wb.pairing, wb.eps)
+    block()
+    torch.cuda.synchronize()
+    be = [ev() for _ in range(4)]
+    be[0].record()
+    for i in range(3):
+        block()
+        be[i + 1].record()
+    torch.cuda.synchronize()
+    t_block = mean([be[i].elapsed_time(be[i + 1]) for i in range(3)]) * 1e-3
+    mt = wb.B * wb.T
+    block_flops = (2.0 * mt * (wb.hidden * wb.q_lora + wb.q_lora * wb.H * wb.Dqk + wb.hidden * (wb.R + wb.Dr) +
+                               wb.H * wb.Dv * wb.hidden) + attn_flops(wb) + expand_flops(wb))
+    del ib
     ms_step = wall * 1e3 / args.steps
     t_prefill = mean(rec["prefill"]) * 1e-3
     t_attn = mean(rec["attn"]) * 1e-3
@@ -299,7 +325,8 @@ def main():
         f"{t_decode * 1e6:.1f} us, decode attention {t_dec_attn * 1e6:.1f} us ({dec_gbs:.0f} GB/s); latent-cache "
         f"decode step {t_lat * 1e6:.1f} us (attention {t_lat_attn * 1e6:.1f} us); chunked prefill (1024 after "
         f"7168) {t_chunk * 1e3:.3f} ms ({chunk_flops / t_chunk / 1e12:.1f} TFLOP/s); latent-cache decode by "
-        f"re-expansion {t_rx * 1e6:.0f} us")
+        f"re-expansion {t_rx * 1e6:.0f} us; attention block (8k) {t_block * 1e3:.3f} ms "
+        f"({block_flops / t_block / 1e12:.1f} TFLOP/s)")
 
     result = {
         "metric": "MLA prefill attn TFLOP/s + % bf16 MFMA peak; decode GB/s at 1k ctx",
@@ -337,6 +364,9 @@ def main():
             "decode_latent_cache_bytes": int(lat_bytes),
             "decode_latent_cache_gbs": round(lat_bytes / t_lat_attn / 1e9, 1),
             "decode_latent_reexpand_attention_us": round(t_rx * 1e6, 1),
+            "block_workload": "attention block at the 8k prefill shape (hidden 7168, q rank 1536, no biases)",
+            "block_ms": round(t_block * 1e3, 4),
+            "block_tflops": round(block_flops / t_block / 1e12, 2),
             "chunked_prefill_workload": f"{PREFILL} last {TQ} tokens after {past} cached rows",
             "chunked_prefill_attention_ms": round(t_chunk * 1e3, 4),
             "chunked_prefill_attention_tflops": round(chunk_flops / t_chunk / 1e12, 2),

@@ -34,7 +34,7 @@ EXPORTS = [
     "mla_rope_table_build", "mla_softmax_scale", "mla_latent_rmsnorm", "mla_kv_expand",
     "mla_prefill_attention", "mla_decode_attention", "mla_absorb_prepare", "mla_latent_cache_append",
     "mla_decode_absorbed", "mla_rotate_rope_key", "mla_prefill_attention_cached", "mla_decode_latent_expanded",
-    "mla_linear", "mla_status_string",
+    "mla_linear", "mla_rmsnorm", "mla_status_string",
 ]
 
 
@@ -95,6 +95,7 @@ def load() -> ctypes.CDLL:
                                                  I32, I32, F32, I32, P, P, P]
     lib.mla_decode_latent_expanded.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, F32, I32,
                                                I32, P, SZ, P, P]
+    lib.mla_rmsnorm.argtypes = [P, P, F32, P, I32, I32, I32, P]
     lib.mla_linear.argtypes = [P, I32, I32, I32, P, P, I32, I32, I32, P, P, I32, I32, I32, I32, P]
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int

@@ -19,7 +19,7 @@ __all__ = [
     "RopeParams", "rope_params", "mla_rope_table_build", "mla_softmax_scale", "mla_latent_rmsnorm",
     "mla_kv_expand", "mla_prefill_attention", "mla_decode_attention", "mla_absorb_prepare",
     "mla_latent_cache_append", "mla_decode_absorbed", "mla_rotate_rope_key", "mla_prefill_attention_cached",
-    "mla_decode_latent_expanded", "mla_linear", "pairing_code",
+    "mla_decode_latent_expanded", "mla_linear", "mla_rmsnorm", "pairing_code",
     "PAIR_HALF", "PAIR_INTERLEAVED", "ROPE_DEFAULT", "ROPE_YARN",
 ]
 
@@ -537,3 +537,21 @@ def mla_linear(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = 
     check("mla_linear", _lib.load().mla_linear(_ptr(x), xl, xT, xD, _ptr(w), _ptr(bias), M, N, K, _ptr(out),
                                                _ptr(y1), yl, yT, yD, ys, _stream(x)))
     return (out, y1) if split is not None else out
+
+
+def mla_rmsnorm(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, dtype=torch.bfloat16,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """RMSNorm of the rows of x [..., R] (bf16) with gain w [R], written in
+    `dtype` (bf16 or fp16)."""
+    _need(x, "x")
+    _need(w, "w")
+    R = x.shape[-1]
+    _shape(w, "w", (R,))
+    if out is None:
+        out = torch.empty(x.shape, dtype=dtype, device=x.device)
+    code = _kv_code(out, "out")
+    _need(out, "out", out.dtype)
+    _shape(out, "out", x.shape)
+    check("mla_rmsnorm", _lib.load().mla_rmsnorm(_ptr(x), _ptr(w), float(eps), _ptr(out), x.numel() // R, R, code,
+                                                 _stream(x)))
+    return out

@@ -124,7 +124,18 @@ mla_status mla_latent_rmsnorm(const mla_bf16* x, const mla_bf16* w, float eps, u
   if (n == 0) return MLA_OK;
   if (!x || !w || !y) return MLA_ERR_NULL;
   clear_stale_error();
-  return hip_status(mla::launch_rmsnorm(x, w, eps, y, n, R, stream));
+  return hip_status(mla::launch_rmsnorm(x, w, eps, y, n, R, MLA_DTYPE_FP16, stream));
+}
+
+mla_status mla_rmsnorm(const mla_bf16* x, const mla_bf16* w, float eps, uint16_t* y, int32_t n, int32_t R,
+                       int32_t out_dtype, hipStream_t stream) {
+  if (!dtype_ok(out_dtype)) return MLA_ERR_UNSUPPORTED;
+  if (n < 0 || R < 1 || R > 8192 || !(eps >= 0.0f) || !isfinite(eps)) return MLA_ERR_SHAPE;
+  if ((int64_t)n * R > kMaxElems) return MLA_ERR_SHAPE;
+  if (n == 0) return MLA_OK;
+  if (!x || !w || !y) return MLA_ERR_NULL;
+  clear_stale_error();
+  return hip_status(mla::launch_rmsnorm(x, w, eps, y, n, R, out_dtype, stream));
 }
 
 mla_status mla_kv_expand(const uint16_t* c_norm, const mla_bf16* W, int32_t B, int32_t T, int32_t R, int32_t H,

@@ -24,7 +24,7 @@ struct RopeResolved {
 hipError_t launch_rope_table(const RopeResolved& r, int n_pos, float* cos_out, float* sin_out,
                              hipStream_t stream);
 
-hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* w, float eps, uint16_t* y, int n, int R,
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* w, float eps, uint16_t* y, int n, int R, int out_dtype,
                           hipStream_t stream);
 
 struct ExpandArgs {

@@ -1,11 +1,13 @@
-// Latent RMSNorm (equation page "Read the equation": kv_a_layernorm of the
+// RMSNorm (equation page "Read the equation": kv_a_layernorm of the
 // compressed latent; GLM-5 "Normalized key-value latent": default epsilon
-// 1e-6). One wavefront per row; 16-byte coalesced bf16 loads; fp32 sum of
-// squares reduced across the wavefront. The normalised latent is written in
-// fp16 (one round-to-nearest-even per element): kv_b_proj multiplies it on
-// fp16 MFMA, and fp16's 11 significant bits keep its rounding at the level
-// of the fp16 keys and values themselves (bf16's 8 bits made it the largest
-// single error of the path).
+// 1e-6; Kimi-K2 "Query content heads": q_a_layernorm between the query
+// projections). One wavefront per row; 16-byte coalesced bf16 loads; fp32 sum
+// of squares reduced across the wavefront; one round-to-nearest-even per
+// element into the output type. The latent is written in fp16: kv_b_proj
+// multiplies it on fp16 MFMA, and fp16's 11 significant bits keep its
+// rounding at the level of the fp16 keys and values themselves (bf16's 8
+// bits made it the largest single error of the path). The query RMSNorm
+// writes bf16, the input type of q_b_proj.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -14,7 +16,7 @@ namespace mla {
 // Rows whose width R is a multiple of 8 and at most 512*NCH: each lane keeps
 // NCH chunks of 8 elements in registers (chunk c of lane l covers columns
 // 8*(l + 64*c) .. +8).
-template <int NCH>
+template <int NCH, class OT>
 __global__ void __launch_bounds__(256) rmsnorm_vec_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                                                           float eps, uint16_t* __restrict__ y, int n, int R) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -51,7 +53,7 @@ __global__ void __launch_bounds__(256) rmsnorm_vec_kernel(const uint16_t* __rest
       for (int j = 0; j < 4; ++j) {
         const float a = __uint_as_float(v[c][j] << 16) * r * __uint_as_float(g[j] << 16);
         const float b = __uint_as_float(v[c][j] & 0xffff0000u) * r * __uint_as_float(g[j] & 0xffff0000u);
-        o[j] = pack2h(a, b);
+        o[j] = OT::pack2(a, b);
       }
       yr[ch] = o;
     }
@@ -59,6 +61,7 @@ __global__ void __launch_bounds__(256) rmsnorm_vec_kernel(const uint16_t* __rest
 }
 
 // Any width: two passes over the row with scalar loads.
+template <class OT>
 __global__ void __launch_bounds__(256) rmsnorm_any_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                                                           float eps, uint16_t* __restrict__ y, int n, int R) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -73,22 +76,31 @@ __global__ void __launch_bounds__(256) rmsnorm_any_kernel(const uint16_t* __rest
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)R + eps);
   uint16_t* yr = y + (size_t)row * R;
-  for (int i = lane; i < R; i += 64) yr[i] = f2h(bf2f(xr[i]) * r * bf2f(w[i]));
+  for (int i = lane; i < R; i += 64) yr[i] = OT::enc(bf2f(xr[i]) * r * bf2f(w[i]));
 }
 
-hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* w, float eps, uint16_t* y, int n, int R,
-                          hipStream_t stream) {
+template <class OT>
+static void launch_rmsnorm_t(const uint16_t* x, const uint16_t* w, float eps, uint16_t* y, int n, int R,
+                             hipStream_t stream) {
   const dim3 grid((n + 3) / 4), block(256);
   const bool aligned = ((((uintptr_t)x) | ((uintptr_t)w) | ((uintptr_t)y)) & 15) == 0;
   if (aligned && (R % 8) == 0 && R <= 512) {
-    hipLaunchKernelGGL(rmsnorm_vec_kernel<1>, grid, block, 0, stream, x, w, eps, y, n, R);
+    hipLaunchKernelGGL((rmsnorm_vec_kernel<1, OT>), grid, block, 0, stream, x, w, eps, y, n, R);
   } else if (aligned && (R % 8) == 0 && R <= 1024) {
-    hipLaunchKernelGGL(rmsnorm_vec_kernel<2>, grid, block, 0, stream, x, w, eps, y, n, R);
+    hipLaunchKernelGGL((rmsnorm_vec_kernel<2, OT>), grid, block, 0, stream, x, w, eps, y, n, R);
   } else if (aligned && (R % 8) == 0 && R <= 4096) {
-    hipLaunchKernelGGL(rmsnorm_vec_kernel<8>, grid, block, 0, stream, x, w, eps, y, n, R);
+    hipLaunchKernelGGL((rmsnorm_vec_kernel<8, OT>), grid, block, 0, stream, x, w, eps, y, n, R);
   } else {
-    hipLaunchKernelGGL(rmsnorm_any_kernel, grid, block, 0, stream, x, w, eps, y, n, R);
+    hipLaunchKernelGGL(rmsnorm_any_kernel<OT>, grid, block, 0, stream, x, w, eps, y, n, R);
   }
+}
+
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* w, float eps, uint16_t* y, int n, int R, int out_dtype,
+                          hipStream_t stream) {
+  if (out_dtype == BF16::code)
+    launch_rmsnorm_t<BF16>(x, w, eps, y, n, R, stream);
+  else
+    launch_rmsnorm_t<F16>(x, w, eps, y, n, R, stream);
   return hipGetLastError();
 }
 

@@ -132,3 +132,19 @@ def prefill_chunk(q, latent, k_pe, gain, W, cache: ChunkCache, past: int, table:
     api.mla_rotate_rope_key(k_pe, table.cos, table.sin, cache.k_rot, past, pairing)
     return api.mla_prefill_attention_cached(q, cache.k_nope, cache.k_rot, cache.vt, past, table.cos, table.sin,
                                             table.scale, pairing, return_lse=return_lse, out=out)
+
+
+def block_forward(hidden, W_qa, gain_q, W_qb, W_kva, gain, W, W_o, table: RopeTable, H: int, Dn: int, Dr: int,
+                  Dv: int, pairing="half", eps: float = 1e-6):
+    """The attention block around the path, from hidden states [B, T, hid]:
+    q = q_b_proj(q_a_layernorm(q_a_proj(h))) written head-major, (latent,
+    rotary key) = kv_a_proj_with_mqa(h) written apart, the prefill path, then
+    o_proj on its head-major output. Returns [B, T, hid] bf16."""
+    B, T, _ = hidden.shape
+    R = W.shape[1]
+    qa = api.mla_linear(hidden, W_qa)
+    qn = api.mla_rmsnorm(qa, gain_q, eps, dtype=torch.bfloat16)
+    q = api.mla_linear(qn, W_qb, out_heads=(H, Dn + Dr))
+    latent, k_pe = api.mla_linear(hidden, W_kva, split=R)
+    o = prefill_forward(q, latent, k_pe, gain, W, table, Dn, Dv, pairing, eps)
+    return api.mla_linear(o, W_o, x_heads=True).view(B, T, W_o.shape[0])

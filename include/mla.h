@@ -386,6 +386,17 @@ mla_status mla_decode_latent_expanded(const mla_bf16* q, const mla_bf16* W, cons
                                       int32_t num_splits, void* workspace, size_t* ws_bytes, mla_bf16* out,
                                       hipStream_t stream);
 
+/* RMSNorm with a choice of output type [K2-query, the MLA constructor:
+ * q_a_layernorm between q_a_proj and q_b_proj; GLM-kv: RMSNorm, default
+ * epsilon 1e-6]: y = w * x / sqrt(mean(x^2) + eps) per row of R values, in
+ * fp32, rounded once into out_dtype (MLA_DTYPE_BF16 for the query RMSNorm,
+ * whose output feeds mla_linear; mla_latent_rmsnorm is this with fp16).
+ * Args: x device bf16 [n, R]; w device bf16 [R]; y device [n, R] of type
+ *   out_dtype. 1 <= R <= 8192; n >= 0 (0 is a no-op).
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP. */
+mla_status mla_rmsnorm(const mla_bf16* x, const mla_bf16* w, float eps, uint16_t* y, int32_t n, int32_t R,
+                       int32_t out_dtype, hipStream_t stream);
+
 /* ---- Projections around the latent attention ----------------------------
  * Linear layer Y = X W^T (+ bias) [K2-query "Split content heads" and the
  * MLA constructor: q_a_proj, q_b_proj, kv_a_proj_with_mqa and o_proj are

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared()
-    assert len(names) == 14
+    assert len(names) == 15
     assert sorted(_lib.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -321,3 +321,14 @@ def test_linear_validation(lib):
     assert linear(lib, M=300000, K=8192) == SHAPE  # M*K >= 2^31
     assert linear(lib, x=FAKE + 8) == SHAPE
     assert linear(lib, bias=FAKE + 2) == SHAPE
+
+
+def test_rmsnorm_dtype_validation(lib):
+    def call(x=FAKE, w=FAKE, eps=1e-6, y=FAKE, n=16, R=1536, dt=0):
+        return lib.mla_rmsnorm(x, w, eps, y, n, R, dt, None)
+    assert call(n=0) == OK
+    assert call(y=None) == NULL
+    assert call(dt=5) == UNSUP
+    assert call(R=0) == SHAPE
+    assert call(R=9000) == SHAPE
+    assert call(eps=-1.0) == SHAPE
