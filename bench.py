@@ -28,6 +28,14 @@ Reported (one JSON line):
   chunked         prefill against a past cache: the last 1024-token chunk of
                   the 8k sequence attending to its 7168 cached rows (timed
                   after the steps, attention call only)
+  other shapes    prefill attention at Kimi-K2 1k (warm, and cold after a
+                  512 MB write that evicts the last-level cache, with its
+                  attainable rate from the HBM roofline) and GLM-5 4k
+  ceilings        what this chip sustains: a streaming HBM read and a dense
+                  fp16 MFMA loop on random operands (the library's
+                  measurement aids), and the vendor bf16 GEMM on random
+                  8192^3 operands; the attention and decode figures are also
+                  given as fractions of these
   cpu_baseline    the fp64 CPU oracle on a bounded sample (--cpu-baseline)
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -308,6 +316,79 @@ def main():
     block_flops = (2.0 * mt * (wb.hidden * wb.q_lora + wb.q_lora * wb.H * wb.Dqk + wb.hidden * (wb.R + wb.Dr) +
                                wb.H * wb.Dv * wb.hidden) + attn_flops(wb) + expand_flops(wb))
     del ib
+
+    def launch_times(fn, n):
+        """Per-launch times (ms) of n back-to-back calls, HIP events on the stream."""
+        fn()
+        torch.cuda.synchronize()
+        e = [ev() for _ in range(n + 1)]
+        e[0].record()
+        for i in range(n):
+            fn()
+            e[i + 1].record()
+        torch.cuda.synchronize()
+        return [e[i].elapsed_time(e[i + 1]) for i in range(n)]
+
+    median = lambda xs: sorted(xs)[len(xs) // 2]  # noqa: E731
+
+    # prefill attention at the other two prefill shapes: Kimi-K2 1k (warm,
+    # and cold after a 512 MB write that evicts the last-level cache) and
+    # GLM-5 4k (Dqk 256, Dv 256, interleaved pairing)
+    shapes = {}
+    for name in ("kimi_k2_1k", "glm5_4k"):
+        w = workloads.WORKLOADS[name]
+        inp = workloads.make_inputs(w, device=dev)
+        b = mla.pipeline.alloc_prefill(w.B, w.T, w.H, w.R, w.Dn, w.Dr, w.Dv, dev)
+        t = mla.pipeline.build_table(mla.api.params_from(w.rope, w.Dr), w.T, w.Dqk, dev)
+        mla.api.mla_latent_rmsnorm(inp["latent"], inp["gain"], w.eps, out=b.c_norm)
+        mla.api.mla_kv_expand(b.c_norm, inp["W"], w.H, w.Dn, w.Dv, k=b.k_nope, v=b.v, v_layout="cols")
+
+        def attn(w=w, inp=inp, b=b, t=t):
+            mla.api.mla_prefill_attention(inp["q"], b.k_nope, inp["k_pe"], b.v, t.cos, t.sin, t.scale, w.pairing,
+                                          out=b.out, workspace=b.workspace, v_layout="cols")
+        rec_s = {"warm_ms": median(launch_times(attn, 20))}
+        if name == "kimi_k2_1k":
+            flush = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
+            cold = []
+            for i in range(10):
+                flush.fill_(i)
+                e0, e1 = ev(), ev()
+                e0.record()
+                attn()
+                e1.record()
+                torch.cuda.synchronize()
+                cold.append(e0.elapsed_time(e1))
+            rec_s["cold_ms"] = median(cold)
+            del flush
+        # algorithmic bytes: q, k_nope, v, out per head and the shared k_pe
+        abytes = 2.0 * w.B * w.H * w.T * (w.Dqk + w.Dn + 2 * w.Dv) + 2.0 * w.B * w.T * w.Dr
+        rec_s["flops"] = attn_flops(w)
+        rec_s["attainable_tflops"] = min(MFMA_PEAK_TFLOPS, attn_flops(w) / abytes * HBM_PEAK_GBS / 1e3)
+        shapes[name] = rec_s
+        del inp, b
+
+    # sustained ceilings of this chip: a streaming HBM read and a dense fp16
+    # MFMA loop on random operands (our own kernels), and the vendor bf16 GEMM
+    # (torch.matmul, hipBLASLt) on random 8192^3 operands as a black box
+    hbm_buf = torch.empty((2 << 30,), dtype=torch.uint8, device=dev).fill_(0x5A)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    hbm_gbs = (2 << 30) / median(launch_times(lambda: mla.api.mla_ceiling_hbm_read(hbm_buf, sink), 10)) / 1e6
+    del hbm_buf
+    gen = torch.Generator(device=dev).manual_seed(11)
+    ops = torch.randn(24576, generator=gen, device=dev).to(torch.float16)
+    fsink = torch.zeros(1, dtype=torch.float32, device=dev)
+    mfma_ceiling = {}
+    for lds in (False, True):
+        fl = [0.0]
+
+        def loop(lds=lds, fl=fl):
+            fl[0] = mla.api.mla_ceiling_mfma(ops, 1000, lds, fsink)
+        t_loop = median(launch_times(loop, 8))  # runs the loop (and sets its flop count) first
+        mfma_ceiling[lds] = fl[0] / t_loop / 1e9
+    ga = torch.randn((8192, 8192), generator=gen, device=dev).to(torch.bfloat16)
+    gb = torch.randn((8192, 8192), generator=gen, device=dev).to(torch.bfloat16)
+    gemm_tflops = 2.0 * 8192 ** 3 / median(launch_times(lambda: torch.matmul(ga, gb), 8)) / 1e9
+    del ga, gb
     ms_step = wall * 1e3 / args.steps
     t_prefill = mean(rec["prefill"]) * 1e-3
     t_attn = mean(rec["attn"]) * 1e-3
@@ -327,6 +408,12 @@ def main():
         f"7168) {t_chunk * 1e3:.3f} ms ({chunk_flops / t_chunk / 1e12:.1f} TFLOP/s); latent-cache decode by "
         f"re-expansion {t_rx * 1e6:.0f} us; attention block (8k) {t_block * 1e3:.3f} ms "
         f"({block_flops / t_block / 1e12:.1f} TFLOP/s)")
+    k1, g4 = shapes["kimi_k2_1k"], shapes["glm5_4k"]
+    log(f"[bench] prefill attention kimi_k2_1k {k1['flops'] / k1['warm_ms'] / 1e9:.1f} TFLOP/s warm, "
+        f"{k1['flops'] / k1['cold_ms'] / 1e9:.1f} cold (attainable {k1['attainable_tflops']:.0f}); glm5_4k "
+        f"{g4['flops'] / g4['warm_ms'] / 1e9:.1f} TFLOP/s; ceilings: HBM read {hbm_gbs:.0f} GB/s, fp16 MFMA on "
+        f"random operands {mfma_ceiling[False]:.0f} TFLOP/s (A from LDS {mfma_ceiling[True]:.0f}), vendor bf16 "
+        f"GEMM 8192^3 {gemm_tflops:.0f} TFLOP/s")
 
     result = {
         "metric": "MLA prefill attn TFLOP/s + % bf16 MFMA peak; decode GB/s at 1k ctx",
@@ -370,6 +457,17 @@ def main():
             "chunked_prefill_workload": f"{PREFILL} last {TQ} tokens after {past} cached rows",
             "chunked_prefill_attention_ms": round(t_chunk * 1e3, 4),
             "chunked_prefill_attention_tflops": round(chunk_flops / t_chunk / 1e12, 2),
+            "prefill_kimi_k2_1k_attention_tflops": round(k1["flops"] / k1["warm_ms"] / 1e9, 2),
+            "prefill_kimi_k2_1k_attention_tflops_cold": round(k1["flops"] / k1["cold_ms"] / 1e9, 2),
+            "prefill_kimi_k2_1k_attainable_tflops": round(k1["attainable_tflops"], 1),
+            "prefill_glm5_4k_attention_tflops": round(g4["flops"] / g4["warm_ms"] / 1e9, 2),
+            "prefill_glm5_4k_mfma_frac": round(g4["flops"] / g4["warm_ms"] / 1e9 / MFMA_PEAK_TFLOPS, 4),
+            "ceiling_hbm_read_gbs": round(hbm_gbs, 1),
+            "ceiling_mfma_f16_random_tflops": round(mfma_ceiling[False], 1),
+            "ceiling_mfma_f16_random_lds_operand_tflops": round(mfma_ceiling[True], 1),
+            "ceiling_vendor_gemm_bf16_random_8192_tflops": round(gemm_tflops, 1),
+            "prefill_attention_frac_of_mfma_ceiling": round(attn_tflops / mfma_ceiling[False], 4),
+            "decode_attention_frac_of_hbm_read_ceiling": round(dec_gbs / hbm_gbs, 4),
             "decode_latent_attn_kernel_traffic_bytes": measured_traffic(
                 "head_latent_attention_rmsnorm_amd/csrc/decode_latent.hip", "decode_latent"),
         },

@@ -36,6 +36,9 @@ EXPORTS = [
     "mla_decode_absorbed", "mla_rotate_rope_key", "mla_prefill_attention_cached", "mla_decode_latent_expanded",
     "mla_linear", "mla_rmsnorm", "mla_status_string",
 ]
+# the measurement aids mla_ceiling.h declares
+CEILING_EXPORTS = ["mla_ceiling_hbm_read", "mla_ceiling_mfma"]
+CEILING_MFMA_OPERAND_BYTES = 49152
 
 
 class RopeParams(ctypes.Structure):
@@ -98,6 +101,10 @@ def load() -> ctypes.CDLL:
     lib.mla_rmsnorm.argtypes = [P, P, F32, P, I32, I32, I32, P]
     lib.mla_linear.argtypes = [P, I32, I32, I32, P, P, I32, I32, I32, P, P, I32, I32, I32, I32, P]
     for name in EXPORTS[:-1]:
+        getattr(lib, name).restype = ctypes.c_int
+    lib.mla_ceiling_hbm_read.argtypes = [P, ctypes.c_size_t, P, P]
+    lib.mla_ceiling_mfma.argtypes = [P, I32, I32, P, ctypes.POINTER(ctypes.c_double), P]
+    for name in CEILING_EXPORTS:
         getattr(lib, name).restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p

@@ -555,3 +555,32 @@ def mla_rmsnorm(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, dtype=torch
     check("mla_rmsnorm", _lib.load().mla_rmsnorm(_ptr(x), _ptr(w), float(eps), _ptr(out), x.numel() // R, R, code,
                                                  _stream(x)))
     return out
+
+
+# ---- measurement aids (mla_ceiling.h): sustained ceilings of the chip
+
+def mla_ceiling_hbm_read(buf: torch.Tensor, sink: torch.Tensor) -> int:
+    """Queue one streaming read of every byte of `buf` (device, contiguous,
+    16-byte aligned, a multiple of 16 bytes); `sink` is a 4-byte device
+    tensor. Returns the bytes read."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if not sink.is_cuda or sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must be a device tensor of at least 4 bytes")
+    n = buf.numel() * buf.element_size()
+    check("mla_ceiling_hbm_read", _lib.load().mla_ceiling_hbm_read(_ptr(buf), n, _ptr(sink), _stream(buf)))
+    return n
+
+
+def mla_ceiling_mfma(operands: torch.Tensor, iters: int, lds_operands: bool, sink: torch.Tensor) -> float:
+    """Queue one dense fp16 MFMA loop over `operands` (fp16 device tensor of
+    24576 values, e.g. random ones); returns the launch's flop count."""
+    _need(operands, "operands", torch.float16)
+    if operands.numel() * 2 != _lib.CEILING_MFMA_OPERAND_BYTES:
+        raise ValueError(f"operands must hold {_lib.CEILING_MFMA_OPERAND_BYTES // 2} fp16 values")
+    if not sink.is_cuda or sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must be a device tensor of at least 4 bytes")
+    flops = ctypes.c_double()
+    check("mla_ceiling_mfma", _lib.load().mla_ceiling_mfma(_ptr(operands), int(iters), int(bool(lds_operands)),
+                                                           _ptr(sink), ctypes.byref(flops), _stream(operands)))
+    return flops.value

@@ -20,7 +20,7 @@ OUT = os.path.join(HERE, "libmla.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["rope_table.hip", "rmsnorm.hip", "kv_expand.hip", "prefill_attn.hip", "decode_attn.hip", "decode_latent.hip",
-           "linear.hip",
+           "linear.hip", "ceiling.hip",
            "api.cpp"]
 
 ARCH = "gfx950"

@@ -332,3 +332,32 @@ def test_rmsnorm_dtype_validation(lib):
     assert call(R=0) == SHAPE
     assert call(R=9000) == SHAPE
     assert call(eps=-1.0) == SHAPE
+
+
+CEILING_HEADER = os.path.join(ROOT, "include", "mla_ceiling.h")
+
+
+def test_ceiling_exports_every_declared_symbol(lib):
+    txt = open(CEILING_HEADER).read()
+    names = sorted(set(re.findall(r"^\s*mla_status\s+(mla_\w+)\s*\(", txt, re.M)))
+    assert names == sorted(_lib.CEILING_EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    m = re.search(r"#define MLA_CEILING_MFMA_OPERAND_BYTES (\d+)", txt)
+    assert m and int(m.group(1)) == _lib.CEILING_MFMA_OPERAND_BYTES
+
+
+def test_ceiling_validation(lib):
+    # every call fails validation: nothing is launched
+    assert lib.mla_ceiling_hbm_read(None, 16, FAKE, None) == NULL
+    assert lib.mla_ceiling_hbm_read(FAKE, 16, None, None) == NULL
+    assert lib.mla_ceiling_hbm_read(FAKE, 0, FAKE, None) == SHAPE
+    assert lib.mla_ceiling_hbm_read(FAKE, 24, FAKE, None) == SHAPE
+    assert lib.mla_ceiling_hbm_read(FAKE + 8, 32, FAKE, None) == SHAPE
+    flops = ctypes.c_double(-1.0)
+    assert lib.mla_ceiling_mfma(None, 1, 0, FAKE, ctypes.byref(flops), None) == NULL
+    assert lib.mla_ceiling_mfma(FAKE, 1, 0, None, ctypes.byref(flops), None) == NULL
+    assert lib.mla_ceiling_mfma(FAKE, 0, 0, FAKE, ctypes.byref(flops), None) == SHAPE
+    assert lib.mla_ceiling_mfma(FAKE, 1, 2, FAKE, ctypes.byref(flops), None) == SHAPE
+    assert lib.mla_ceiling_mfma(FAKE + 8, 1, 0, FAKE, ctypes.byref(flops), None) == SHAPE
+    assert flops.value == -1.0
