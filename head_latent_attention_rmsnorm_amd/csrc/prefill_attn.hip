@@ -37,7 +37,9 @@
 //    consecutive keys: P goes from the S accumulator to a 16-bit B operand of
 //    O^T = V^T P^T with no data movement;
 //  - all K fragments of a sub-tile are read from LDS before its MFMAs start
-//    (a scheduling fence keeps them in flight together);
+//    (a scheduling fence keeps them in flight together); with a 256-wide
+//    head they are read in four batches, which keeps the kernel within 256
+//    registers (two waves per SIMD);
 //  - each 64-key tile is software-pipelined over its two 32-key sub-tiles:
 //    the score MFMAs of sub-tile 1 are issued ahead of the softmax of
 //    sub-tile 0, and the PV MFMAs of sub-tile 0 ahead of the softmax of
@@ -45,7 +47,9 @@
 //  - MFMA and VALU work hardly overlap on this chip, so the softmax is cut to
 //    the bone: in fp16 mode the query is pre-scaled by scale*log2(e) and the
 //    first MFMA of every score chain accumulates onto -m (the running
-//    reference maximum), so the scores leave the MFMA as exp2 arguments. The
+//    reference maximum), so the scores leave the MFMA as exp2 arguments
+//    (for 256-wide values, where registers rather than VALU issue are the
+//    limit, -m is subtracted on the VALU instead). The
 //    reference only moves when a sub-tile's P would leave a safe range: the
 //    per-lane sum of the sub-tile's P (taken anyway, with v_dot2 on the
 //    packed 16-bit P that the PV product consumes) bounds every P, and only
@@ -92,7 +96,11 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
   constexpr int NBLK = KBLK + NO * NPV; // K + V^T operand blocks per tile
   constexpr int LPW = (NBLK + NW - 1) / NW;  // LDS-direct loads per wave per tile
   constexpr int BMW = NW * 32;          // query rows per workgroup
-  constexpr bool FOLD = ET::code == F16::code;  // scores leave the MFMA as exp2 arguments
+  constexpr bool FOLD = ET::code == F16::code;  // scores leave the MFMA in log2 units (query pre-scaled)
+  // with FOLD, the score chains accumulate onto -m_ref (no subtraction on the
+  // VALU) unless registers are the limit (wide values), where a 16-register
+  // broadcast of -m_ref would spill
+  constexpr bool NEGM = FOLD && DV < 256;
   // k-steps per operand group (see frag_read0): K groups must not straddle
   // the nope|rope boundary
   constexpr int SWK = (DN % 64 == 0 && DR % 64 == 0) ? 4 : (DN % 32 == 0 && DR % 32 == 0) ? 2 : 1;
@@ -290,19 +298,38 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
     f32x16 sacc[NSUB];
     u32x4 pf[NPV];
     auto s_chain = [&](int j) __attribute__((always_inline)) {
-      u32x4 kf[QC];
+      constexpr int KB = QC > 12 ? QC / 4 : QC;  // fragments read ahead of their products
 #pragma unroll
-      for (int c = 0; c < QC; ++c) kf[c] = kfrag(j, c);
-      __builtin_amdgcn_sched_barrier(0);
-      sacc[j] = ET::mma(kf[0], qf[0], negm);
+      for (int c0 = 0; c0 < QC; c0 += KB) {
+        u32x4 kf[KB];
 #pragma unroll
-      for (int c = 1; c < QC; ++c) sacc[j] = ET::mma(kf[c], qf[c], sacc[j]);
+        for (int c = 0; c < KB; ++c) kf[c] = kfrag(j, c0 + c);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < KB; ++c) {
+          if (c0 + c == 0) {
+            if (NEGM) {
+              sacc[j] = ET::mma(kf[c], qf[0], negm);
+            } else {
+              f32x16 z;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) z[i] = 0.f;
+              sacc[j] = ET::mma(kf[c], qf[0], z);
+            }
+          } else {
+            sacc[j] = ET::mma(kf[c], qf[c0 + c], sacc[j]);
+          }
+        }
+      }
     };
     // scale (bf16 mode) and mask the scores of sub-tile j
     auto finish = [&](int j) __attribute__((always_inline)) {
       if (!FOLD) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[j][i] = fmaf(sacc[j][i], sl2, -m_ref);
+      } else if (!NEGM) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[j][i] -= m_ref;
       }
       if (diag) {
 #pragma unroll
@@ -358,7 +385,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
           for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[j][i] -= shift;
-        if (FOLD) {
+        if (NEGM) {
           // the next sub-tile's scores were accumulated onto the old -m_ref
           if (j + 1 < NSUB) {
 #pragma unroll
@@ -479,7 +506,10 @@ template <class ET>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
   const int Dqk = a.Dn + a.Dr;
   if (Dqk == 192 && a.Dv == 128) return launch_one<ET, 192, 64, 128, 64, 8, 2>(a, stream);
-  if (Dqk == 256 && a.Dv == 256) return launch_one<ET, 256, 64, 256, 32, 4, 1>(a, stream);
+  // wide values: 4-wave workgroups at two waves per SIMD (two workgroups per
+  // compute unit); the 256-register budget holds with key fragments read in
+  // batches of four and no -m_ref broadcast
+  if (Dqk == 256 && a.Dv == 256) return launch_one<ET, 256, 64, 256, 32, 4, 2>(a, stream);
   if (Dqk == 48 && a.Dv == 32) return launch_one<ET, 48, 16, 32, 64, 4, 2>(a, stream);
   return hipErrorInvalidValue;
 }
