@@ -266,6 +266,26 @@ def test_prefill_kimi_8k_sampled():
         assert_close(f64(out[b, h])[rows], ref, f"kimi 8k b={b} h={h} ({len(rows)} rows)")
 
 
+def test_prefill_long_context_sampled():
+    """A long sequence with a ragged tail (T = 49999: 196 query tiles, the last
+    one partial, up to 782 key tiles per wave) against the oracle on sampled
+    rows of both heads, the first, the last and random ones: the key loop,
+    the per-slice offsets and the YaRN table at positions far past the
+    original 4096-token context."""
+    w = workloads.custom(name="k2-long", B=1, T=49999, H=2, R=512, Dn=128, Dr=64, Dv=128, seed=36,
+                         rope=workloads.YARN_KIMI)
+    say(f"[prefill] long context B=1 T={w.T} H=2, sampled rows")
+    inp = workloads.make_inputs(w)
+    out = run_prefill(w, inp).cpu()
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.r_[0:64, w.T - 64:w.T, rng.integers(0, w.T, 128)])
+    for h in range(w.H):
+        wh, sub = head_view(w, inp, h)
+        parts = O.prefill_parts(wh, sub)
+        ref = O.prefill_head(wh, parts, 0, 0, rows=rows)
+        assert_close(f64(out[0, h])[rows], ref, f"long context h={h} ({len(rows)} rows)")
+
+
 RAGGED = [
     workloads.custom(name="k2-ragged", B=2, T=300, H=3, R=512, Dn=128, Dr=64, Dv=128, seed=31, rope=workloads.YARN_KIMI),
     workloads.custom(name="k2-one-token", B=2, T=1, H=2, R=512, Dn=128, Dr=64, Dv=128, seed=32, rope=workloads.YARN_KIMI),
