@@ -11,7 +11,10 @@
 //  - workgroup = (sequence b, head h, NW*32 query rows), NW waves of 32 rows;
 //    with 8 waves the row blocks are dealt so that the two waves sharing a
 //    SIMD (w and w+4) get blocks s and 7-s, which evens out the triangular
-//    work of the diagonal tiles;
+//    work of the diagonal tiles. When the grid is a single round (at most
+//    one 8-wave workgroup per compute unit: short sequences), a workgroup
+//    instead takes two 128-row blocks i and nb-1-i (waves 0-3 and 4-7), so
+//    every workgroup carries the same causal work;
 //  - each wave keeps its 32 rotated query rows in registers as the B operand
 //    of S^T = K Q^T, so the score accumulator has one query per lane and the
 //    softmax statistics are per-lane values (lane l and l^32 share a query);
@@ -86,7 +89,7 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, 
 }  // namespace
 
 template <class ET, int DQK, int DR, int DV, int BN, int NW, int MINW>
-__global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, int nqt) {
+__global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, int nqt, int paired) {
   constexpr int DN = DQK - DR;
   constexpr int QC = DQK / 16;          // 16-deep MFMA steps over the head dim
   constexpr int NSUB = BN / 32;         // 32-key sub-tiles
@@ -131,7 +134,20 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
   // 32-row block of this wave; with 8 waves the blocks are dealt so that the
   // waves sharing a SIMD (w and w+4) get blocks s and 7-s, which evens out
   // the triangular work of the diagonal tiles
-  const int qlo = qt * BMW + ((NW == 8 && wave >= 4) ? 11 - wave : wave) * 32;
+  // paired mode (8 waves): work item qt holds two 128-row blocks, qt and
+  // nb-1-qt; waves 0-3 take the first, waves 4-7 the second, so the two waves
+  // sharing a SIMD have complementary causal work and every item the same
+  // total. With an odd block count the middle item's second half is empty.
+  const int nb128 = (T + 127) / 128;
+  bool empty = false;
+  int qlo;
+  if (NW == 8 && paired) {
+    const int blk = wave < 4 ? qt : nb128 - 1 - qt;
+    empty = wave >= 4 && blk == qt;
+    qlo = empty ? T : blk * 128 + (wave & 3) * 32;
+  } else {
+    qlo = qt * BMW + ((NW == 8 && wave >= 4) ? 11 - wave : wave) * 32;
+  }
   const int tq = qlo + l32;  // this lane's query row
   const float sl2 = a.scale * kLog2e;
   const float qmul = FOLD ? sl2 : 1.0f;  // query pre-scale
@@ -199,7 +215,8 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
   }
 
 
-  const int kend = min(Tk, past + (qt + 1) * BMW);  // keys [0, kend) are visible to some row
+  // keys [0, kend) are visible to some row of the work item
+  const int kend = (NW == 8 && paired) ? min(Tk, past + (nb128 - qt) * 128) : min(Tk, past + (qt + 1) * BMW);
   const int nkt = (kend + BN - 1) / BN;
 
   // Key (within a 32-key sub-tile) of operand row r of the S^T MFMA: the
@@ -414,7 +431,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
     const int cur = kt & 1;
     if (kt + 1 < nkt) issue(kt + 1, cur ^ 1);
     const int key0 = kt * BN;
-    if (key0 <= past + qlo + 31) tile(cur, key0);  // some key of the tile is visible to this wave
+    if (!empty && key0 <= past + qlo + 31) tile(cur, key0);  // some key of the tile is visible to this wave
     // the next tile's loads have landed in LDS and every wave is done with
     // this tile's buffer
     __builtin_amdgcn_s_waitcnt(0);
@@ -495,10 +512,14 @@ bool prefill_supported(int Dqk, int Dr, int Dv) {
 template <class ET, int DQK, int DR, int DV, int BN, int NW, int MINW>
 static hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
   constexpr int BMW = NW * 32;
-  const int nqt = (a.T + BMW - 1) / BMW;
   const int hb8 = (a.H * a.B + 7) / 8 * 8;  // (b, h) pairs padded to the XCD count
+  // one round of 8-wave workgroups at most (every workgroup starts at once):
+  // pair 128-row blocks so that all work items carry the same causal work;
+  // with more rounds the heaviest-first order balances better and loads less
+  const int paired = (NW == 8 && (int64_t)a.B * a.H * ((a.T + BMW - 1) / BMW) <= 256) ? 1 : 0;
+  const int nqt = paired ? ((a.T + 127) / 128 + 1) / 2 : (a.T + BMW - 1) / BMW;
   hipLaunchKernelGGL((prefill_kernel<ET, DQK, DR, DV, BN, NW, MINW>), dim3((unsigned)nqt * hb8), dim3(64 * NW), 0,
-                     stream, a, nqt);
+                     stream, a, nqt, paired);
   return hipGetLastError();
 }
 
