@@ -215,7 +215,7 @@ __global__ void __launch_bounds__(512, 2) linear_kernel(LinearArgs a, int nmt, i
     } else {
       dst = n < a.ys ? a.y0 + (size_t)m * a.ys + n : a.y1 + (size_t)m * (N - a.ys) + (n - a.ys);
     }
-    *reinterpret_cast<u32x4*>(dst) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));  // written once: nontemporal
   }
 }
 
