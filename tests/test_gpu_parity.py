@@ -286,6 +286,49 @@ def test_prefill_long_context_sampled():
         assert_close(f64(out[0, h])[rows], ref, f"long context h={h} ({len(rows)} rows)")
 
 
+def test_prefill_explicit_positions():
+    """Positions passed in (pos [B, T]) instead of 0..T-1: each sequence
+    starts at its own offset (0 and 500), so the rotation angles differ from
+    the index while the causal mask, which follows the index, matches the
+    oracle's position mask (positions increase with the index)."""
+    w = workloads.custom(name="k2-pos", B=2, T=300, H=3, R=512, Dn=128, Dr=64, Dv=128, seed=37,
+                         rope=workloads.YARN_KIMI)
+    say("[prefill] explicit positions, offsets 0 and 500")
+    inp = workloads.make_inputs(w)
+    off = np.array([0, 500])
+    pos = np.arange(w.T)[None, :] + off[:, None]  # [B, T]
+    n_pos = int(pos.max()) + 1
+    g = to_gpu(inp)
+    tab = pipeline.build_table(api.params_from(w.rope, w.Dr), n_pos, w.Dqk)
+    c = api.mla_latent_rmsnorm(g["latent"], g["gain"], w.eps)
+    kn, v = api.mla_kv_expand(c, g["W"], w.H, w.Dn, w.Dv, v_layout="cols")
+    out = api.mla_prefill_attention(g["q"], kn, g["k_pe"], v, tab.cos, tab.sin, tab.scale, w.pairing,
+                                    pos=torch.tensor(pos, dtype=torch.int32, device="cuda"), v_layout="cols")
+    torch.cuda.synchronize()
+    got = f64(out.cpu())
+    # oracle: the plain steps with the rotation taken at pos
+    cn = O.rmsnorm(f64(inp["latent"]), f64(inp["gain"]), w.eps)
+    k_nope, vv = O.kv_expand(cn, f64(inp["W"]), w.H, w.Dn, w.Dv)
+    cos, sin = O.rope_table(w.rope, w.Dr, n_pos)
+    q = f64(inp["q"])
+    scale = O.softmax_scale(w.rope, w.Dqk)
+    ref = np.empty_like(got)
+    for b in range(w.B):
+        cb, sb = cos[pos[b]], sin[pos[b]]
+        q_pe = O.rotate(q[b, :, :, w.Dn:], cb[None], sb[None], w.pairing)
+        k_pe = O.rotate(f64(inp["k_pe"])[b], cb, sb, w.pairing)
+        for h in range(w.H):
+            Q = np.concatenate([q[b, h, :, :w.Dn], q_pe[h]], axis=-1)
+            K = np.concatenate([k_nope[b, h], k_pe], axis=-1)
+            ref[b, h] = O.attention(Q, K, vv[b, h], scale, pos[b], pos[b])
+    assert_close(got, ref, "explicit positions")
+    # and the offset matters: positions 0..T-1 give a different result for b = 1
+    plain = api.mla_prefill_attention(g["q"], kn, g["k_pe"], v, tab.cos, tab.sin, tab.scale, w.pairing,
+                                      v_layout="cols")
+    torch.cuda.synchronize()
+    assert np.abs(f64(plain.cpu())[1] - got[1]).max() > 1e-2
+
+
 RAGGED = [
     workloads.custom(name="k2-ragged", B=2, T=300, H=3, R=512, Dn=128, Dr=64, Dv=128, seed=31, rope=workloads.YARN_KIMI),
     workloads.custom(name="k2-one-token", B=2, T=1, H=2, R=512, Dn=128, Dr=64, Dv=128, seed=32, rope=workloads.YARN_KIMI),
