@@ -134,13 +134,14 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
 
   const int l32 = lane & 31;
   const int g = lane >> 5;
-  // 32-row block of this wave; with 8 waves the blocks are dealt so that the
-  // waves sharing a SIMD (w and w+4) get blocks s and 7-s, which evens out
-  // the triangular work of the diagonal tiles
-  // paired mode (8 waves): work item qt holds two 128-row blocks, qt and
-  // nb-1-qt; waves 0-3 take the first, waves 4-7 the second, so the two waves
-  // sharing a SIMD have complementary causal work and every item the same
-  // total. With an odd block count the middle item's second half is empty.
+  // This wave's 32 query rows. Default: work item qt is rows qt*BMW.., and
+  // with 8 waves the 32-row blocks are dealt so that the waves sharing a SIMD
+  // (w and w+4) get blocks s and 7-s, which evens out the triangular work of
+  // the diagonal tiles. Paired mode (8 waves, single-round grids): work item
+  // qt holds two 128-row blocks, qt and nb-1-qt; waves 0-3 take the first,
+  // waves 4-7 the second, so the two waves sharing a SIMD have complementary
+  // causal work and every item the same total. With an odd block count the
+  // middle item's second half is empty (no tiles, no stores).
   const int nb128 = (T + 127) / 128;
   bool empty = false;
   int qlo;
@@ -447,6 +448,8 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
   const float ltot = lsum + __shfl_xor(lsum, 32, 64);
   {
     constexpr int CPR = DV / 8;  // 16-byte chunks per output row
+    static_assert((CPR & (CPR - 1)) == 0 && CPR <= 64, "row swizzle needs a power-of-two chunk count");
+    static_assert(NW * 32 * DV * 2 <= (int)sizeof(smem), "the output tiles fit in the tile buffers");
     char* stile = reinterpret_cast<char*>(&smem[0][0]) + wave * (32 * DV * 2);
     const float inv = 1.0f / ltot;
 #pragma unroll
