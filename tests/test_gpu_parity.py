@@ -432,6 +432,23 @@ def test_prefill_properties():
     assert_close(f64(z), mean, "q=0 prefix mean", max_abs=2e-2, rel_l2=5e-3)
 
 
+@pytest.mark.parametrize("qmul", [3.0, 4.5])
+def test_prefill_sharp_softmax(qmul):
+    """A peaked softmax: the query scaled up so that scores span many powers
+    of two and later key tiles keep overtaking the running maximum (the
+    kernel's reference moves when a sub-tile's P would leave the safe range,
+    and P is first formed against a stale reference). Compared with the oracle
+    on the same scaled inputs."""
+    w = workloads.custom(name="k2-sharp", B=1, T=700, H=2, R=512, Dn=128, Dr=64, Dv=128, seed=38,
+                         rope=workloads.YARN_KIMI)
+    say(f"[prefill] sharp softmax, q x {qmul}")
+    inp = workloads.make_inputs(w)
+    inp["q"] = (inp["q"].float() * qmul).to(torch.bfloat16)
+    out = run_prefill(w, inp)
+    assert torch.isfinite(out.float()).all()
+    assert_close(f64(out.cpu()), O.prefill(w, inp), f"sharp softmax q x {qmul}")
+
+
 # --------------------------------------------------------------------- decode
 
 def run_decode(w, g, num_splits=0):
