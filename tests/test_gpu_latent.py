@@ -129,6 +129,22 @@ def test_decode_absorbed_single_row_and_padding():
         assert_close(f64(out), ref, f"absorbed single-row splits={S}")
 
 
+@pytest.mark.parametrize("qmul", [3.0, 4.5])
+def test_decode_absorbed_sharp_softmax(qmul):
+    # the query scaled up: scores span many powers of two, so later key tiles
+    # overtake the per-head reference (the lazy rescale path)
+    w = small(seed=46, B=2, L=400)
+    inp = workloads.make_inputs(w)
+    inp["q"] = (inp["q"].float() * qmul).to(torch.bfloat16)
+    q_pos = [399, 250]
+    ref = O.decode_latent(w, inp, q_pos=q_pos)
+    for S in (0, 1, 3):
+        say(f"[latent] sharp softmax q x {qmul} splits={S}")
+        out, _ = run(w, inp, q_pos, S)
+        assert np.all(np.isfinite(f64(out)))
+        assert_close(f64(out), ref, f"absorbed sharp x{qmul} splits={S}")
+
+
 def test_decode_absorbed_kimi():
     w = workloads.WORKLOADS["kimi_k2_decode_latent"]
     say("[latent] kimi_k2_decode_latent B=32 L=1001 H=64")
