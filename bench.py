@@ -20,6 +20,7 @@ Reported (one JSON line):
                   against the MI355X dense 16-bit MFMA peak
   decode          decode attention GB/s (algorithmic bytes) and HBM fraction
   decode_latent   step time of the latent-cache decode and its attention
+  graphs          both decode steps recorded once as HIP graphs and replayed
   decode_latent_reexpand  the same latent-cache decode by re-expanding every
                   cached row on each call (timed after the steps)
   block           the whole attention block at the 8k prefill shape (hidden
@@ -367,6 +368,30 @@ def main():
         shapes[name] = rec_s
         del inp, b
 
+    # the two decode steps recorded once as HIP graphs and replayed (the same
+    # calls as in the timed steps, table build included): launch-bound steps
+    def dec_step():
+        td = mla.pipeline.build_table(rope_d, wd.cache_len, wd.Dqk, dev)
+        mla.api.mla_latent_rmsnorm(idc["latent"], idc["gain"], wd.eps, out=c_dec)
+        mla.api.mla_kv_expand(c_dec, idc["W"], wd.H, wd.Dn, wd.Dv, k=idc["k_cache"], v=idc["v_cache"],
+                              t_off=wd.q_pos, k_pe=idc["k_pe"], cos=td.cos, sin=td.sin, pos=qpos.view(-1, 1),
+                              pairing=wd.pairing)
+        return mla.api.mla_decode_attention(idc["q"], idc["k_cache"], idc["v_cache"], seq, qpos, td.cos, td.sin,
+                                            td.scale, wd.Dn, wd.pairing, splits, out=out_dec, workspace=ws_dec)
+
+    def lat_step():
+        tl = mla.pipeline.build_table(rope_l, wl.cache_len, wl.Dqk, dev)
+        mla.api.mla_latent_cache_append(il["latent"].view(wl.B, wl.R), il["gain"], il["k_pe"].view(wl.B, wl.Dr),
+                                        tl.cos, tl.sin, qpos_l, il["latent_cache"], wl.eps, wl.pairing)
+        return mla.api.mla_decode_absorbed(il["q"], il["W"], w_ukt, il["latent_cache"], seq_l, qpos_l, tl.cos,
+                                           tl.sin, tl.scale, wl.Dn, wl.Dv, wl.pairing, 0, out=out_lat,
+                                           workspace=ws_lat)
+    g_dec = mla.pipeline.StepGraph(dec_step)
+    g_lat = mla.pipeline.StepGraph(lat_step)
+    t_dec_graph = median(launch_times(g_dec.replay, 20)) * 1e-3
+    t_lat_graph = median(launch_times(g_lat.replay, 20)) * 1e-3
+    del g_dec, g_lat
+
     # sustained ceilings of this chip: a streaming HBM read and a dense fp16
     # MFMA loop on random operands (our own kernels), and the vendor bf16 GEMM
     # (torch.matmul, hipBLASLt) on random 8192^3 operands as a black box
@@ -408,6 +433,8 @@ def main():
         f"7168) {t_chunk * 1e3:.3f} ms ({chunk_flops / t_chunk / 1e12:.1f} TFLOP/s); latent-cache decode by "
         f"re-expansion {t_rx * 1e6:.0f} us; attention block (8k) {t_block * 1e3:.3f} ms "
         f"({block_flops / t_block / 1e12:.1f} TFLOP/s)")
+    log(f"[bench] decode steps replayed as HIP graphs: expanded cache {t_dec_graph * 1e6:.1f} us, latent cache "
+        f"{t_lat_graph * 1e6:.1f} us")
     k1, g4 = shapes["kimi_k2_1k"], shapes["glm5_4k"]
     log(f"[bench] prefill attention kimi_k2_1k {k1['flops'] / k1['warm_ms'] / 1e9:.1f} TFLOP/s warm, "
         f"{k1['flops'] / k1['cold_ms'] / 1e9:.1f} cold (attainable {k1['attainable_tflops']:.0f}); glm5_4k "
@@ -451,6 +478,8 @@ def main():
             "decode_latent_cache_bytes": int(lat_bytes),
             "decode_latent_cache_gbs": round(lat_bytes / t_lat_attn / 1e9, 1),
             "decode_latent_reexpand_attention_us": round(t_rx * 1e6, 1),
+            "decode_step_graph_us": round(t_dec_graph * 1e6, 2),
+            "decode_latent_step_graph_us": round(t_lat_graph * 1e6, 2),
             "block_workload": "attention block at the 8k prefill shape (hidden 7168, q rank 1536, no biases)",
             "block_ms": round(t_block * 1e3, 4),
             "block_tflops": round(block_flops / t_block / 1e12, 2),

@@ -148,3 +148,31 @@ def block_forward(hidden, W_qa, gain_q, W_qb, W_kva, gain, W, W_o, table: RopeTa
     latent, k_pe = api.mla_linear(hidden, W_kva, split=R)
     o = prefill_forward(q, latent, k_pe, gain, W, table, Dn, Dv, pairing, eps)
     return api.mla_linear(o, W_o, x_heads=True).view(B, T, W_o.shape[0])
+
+
+class StepGraph:
+    """A step recorded once as a HIP graph (torch.cuda.CUDAGraph) and replayed:
+    for launch-bound steps such as a decode step, whose kernels are short and
+    serially dependent. `step` is a callable that issues the library's calls
+    on the current stream and returns its output tensor; every tensor it
+    reads or writes must stay allocated and at the same address (fill new
+    inputs into them before `replay`), and its output (allocated during
+    capture from the graph's private pool) is overwritten by each replay. The
+    library queues no memset and no host synchronisation, so its calls can
+    be recorded."""
+
+    def __init__(self, step, warmup: int = 2):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.output = step()
+
+    def replay(self):
+        self.graph.replay()
+        return self.output
