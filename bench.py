@@ -414,6 +414,12 @@ def main():
     gb = torch.randn((8192, 8192), generator=gen, device=dev).to(torch.bfloat16)
     gemm_tflops = 2.0 * 8192 ** 3 / median(launch_times(lambda: torch.matmul(ga, gb), 8)) / 1e9
     del ga, gb
+    # the chip at hand: compute units and peak clocks as the runtime reports
+    # them, and the dense 16-bit MFMA rate they imply (4096 flop/clk per CU)
+    device = mla.api.mla_device_info(0)
+    device["arch"] = torch.cuda.get_device_properties(0).gcnArchName
+    device["mfma_f16_peak_at_peak_sclk_tflops"] = round(
+        device["compute_units"] * 4096 * device["peak_sclk_mhz"] * 1e6 / 1e12, 1)
     ms_step = wall * 1e3 / args.steps
     t_prefill = mean(rec["prefill"]) * 1e-3
     t_attn = mean(rec["attn"]) * 1e-3
@@ -491,6 +497,7 @@ def main():
             "prefill_kimi_k2_1k_attainable_tflops": round(k1["attainable_tflops"], 1),
             "prefill_glm5_4k_attention_tflops": round(g4["flops"] / g4["warm_ms"] / 1e9, 2),
             "prefill_glm5_4k_mfma_frac": round(g4["flops"] / g4["warm_ms"] / 1e9 / MFMA_PEAK_TFLOPS, 4),
+            "device": device,
             "ceiling_hbm_read_gbs": round(hbm_gbs, 1),
             "ceiling_mfma_f16_random_tflops": round(mfma_ceiling[False], 1),
             "ceiling_mfma_f16_random_lds_operand_tflops": round(mfma_ceiling[True], 1),

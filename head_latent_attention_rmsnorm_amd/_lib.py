@@ -37,7 +37,7 @@ EXPORTS = [
     "mla_linear", "mla_rmsnorm", "mla_status_string",
 ]
 # the measurement aids mla_ceiling.h declares
-CEILING_EXPORTS = ["mla_ceiling_hbm_read", "mla_ceiling_mfma"]
+CEILING_EXPORTS = ["mla_ceiling_hbm_read", "mla_ceiling_mfma", "mla_device_info"]
 CEILING_MFMA_OPERAND_BYTES = 49152
 
 
@@ -104,6 +104,7 @@ def load() -> ctypes.CDLL:
         getattr(lib, name).restype = ctypes.c_int
     lib.mla_ceiling_hbm_read.argtypes = [P, ctypes.c_size_t, P, P]
     lib.mla_ceiling_mfma.argtypes = [P, I32, I32, P, ctypes.POINTER(ctypes.c_double), P]
+    lib.mla_device_info.argtypes = [I32, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]
     for name in CEILING_EXPORTS:
         getattr(lib, name).restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]

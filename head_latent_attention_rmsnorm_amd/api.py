@@ -584,3 +584,11 @@ def mla_ceiling_mfma(operands: torch.Tensor, iters: int, lds_operands: bool, sin
     check("mla_ceiling_mfma", _lib.load().mla_ceiling_mfma(_ptr(operands), int(iters), int(bool(lds_operands)),
                                                            _ptr(sink), ctypes.byref(flops), _stream(operands)))
     return flops.value
+
+
+def mla_device_info(device: int = 0) -> dict:
+    """Compute units and peak shader / memory clocks (MHz) of a device."""
+    cu, sclk, mclk = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    check("mla_device_info", _lib.load().mla_device_info(int(device), ctypes.byref(cu), ctypes.byref(sclk),
+                                                         ctypes.byref(mclk)))
+    return {"compute_units": cu.value, "peak_sclk_mhz": sclk.value / 1000.0, "peak_mclk_mhz": mclk.value / 1000.0}

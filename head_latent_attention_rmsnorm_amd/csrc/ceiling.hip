@@ -101,3 +101,17 @@ extern "C" mla_status mla_ceiling_mfma(const uint16_t* operands, int32_t iters, 
   }
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
+
+extern "C" mla_status mla_device_info(int32_t device, int32_t* compute_units, int32_t* peak_sclk_khz,
+                                      int32_t* peak_mclk_khz) {
+  if (!compute_units || !peak_sclk_khz || !peak_mclk_khz) return MLA_ERR_NULL;
+  int cu = 0, sclk = 0, mclk = 0;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+      hipDeviceGetAttribute(&sclk, hipDeviceAttributeClockRate, device) != hipSuccess ||
+      hipDeviceGetAttribute(&mclk, hipDeviceAttributeMemoryClockRate, device) != hipSuccess)
+    return MLA_ERR_HIP;
+  *compute_units = cu;
+  *peak_sclk_khz = sclk;
+  *peak_mclk_khz = mclk;
+  return MLA_OK;
+}

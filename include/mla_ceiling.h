@@ -54,6 +54,15 @@ mla_status mla_ceiling_hbm_read(const void* buf, size_t bytes, uint32_t* sink, h
 mla_status mla_ceiling_mfma(const uint16_t* operands, int32_t iters, int32_t lds_operands, float* sink,
                             double* flops, hipStream_t stream);
 
+/*
+ * The device's compute-unit count and peak shader and memory clocks (kHz), as
+ * the HIP runtime reports them, for reading the published peaks against the
+ * chip at hand (dense 16-bit MFMA: 4096 flop per clock per compute unit).
+ * All outputs are host pointers. Errors: MLA_ERR_NULL, MLA_ERR_HIP (an
+ * invalid device or a runtime failure).
+ */
+mla_status mla_device_info(int32_t device, int32_t* compute_units, int32_t* peak_sclk_khz, int32_t* peak_mclk_khz);
+
 #ifdef __cplusplus
 }
 #endif

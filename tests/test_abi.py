@@ -361,3 +361,5 @@ def test_ceiling_validation(lib):
     assert lib.mla_ceiling_mfma(FAKE, 1, 2, FAKE, ctypes.byref(flops), None) == SHAPE
     assert lib.mla_ceiling_mfma(FAKE + 8, 1, 0, FAKE, ctypes.byref(flops), None) == SHAPE
     assert flops.value == -1.0
+    v = ctypes.c_int32()
+    assert lib.mla_device_info(0, None, ctypes.byref(v), ctypes.byref(v)) == NULL

@@ -32,3 +32,10 @@ def test_mfma_loop_runs(lds):
     torch.cuda.synchronize()
     assert flops == 12 * (2 if lds else 4) * 32768 * 3 * 8 * 512
     assert sink.item() == 0.0
+
+
+def test_device_info():
+    info = api.mla_device_info(0)
+    say(f"[ceiling] device info {info}")
+    assert info["compute_units"] == torch.cuda.get_device_properties(0).multi_processor_count
+    assert info["peak_sclk_mhz"] > 0 and info["peak_mclk_mhz"] > 0
