@@ -165,6 +165,13 @@ __global__ void __launch_bounds__(512, 2) expand_tile_kernel(ExpandArgs a, int M
     const size_t row = n < N ? (size_t)h * (a.Dn + a.Dv) + (VPART ? a.Dn : 0) + (n - h * D) : 0;
     wrow[j] = a.W + row * R + ((tid + 512 * j) % CPR) * 8;
   }
+  // W fragment slots are XOR-permuted: slot (row r, 8-element chunk kc of
+  // the stage) sits at (r ^ 4kc) + 32(kc & 1) of its k-step's block. The four
+  // threads that load one row's four chunks then store to four different
+  // bank groups (without the permutation they hit the same one, a 4-way
+  // conflict), and an operand read (16 lanes, 16 consecutive rows, one
+  // chunk) still covers all 16 bank groups.
+  auto wslot = [](int r, int kc) __attribute__((always_inline)) { return (r ^ (4 * kc)) + 32 * (kc & 1); };
   // W chunks of the stages in flight are held in registers, one set per
   // stage buffer (the stage loop is unrolled by XT_NB so the set is static)
   u32x4 wreg[XT_NB][WPT];
@@ -178,7 +185,7 @@ __global__ void __launch_bounds__(512, 2) expand_tile_kernel(ExpandArgs a, int M
       const int id = tid + 512 * j;
       const int nl = id / CPR, kc = id % CPR;
       const int blk = XT_BLK + (nl >> 5) * KS + (kc >> 1);
-      smem[set][blk * 64 + (nl & 31) + 32 * (kc & 1)] = bf16x8_to_f16x8(wreg[set][j]);
+      smem[set][blk * 64 + wslot(nl & 31, kc)] = bf16x8_to_f16x8(wreg[set][j]);
     }
   };
 
@@ -219,13 +226,14 @@ __global__ void __launch_bounds__(512, 2) expand_tile_kernel(ExpandArgs a, int M
     }
     if (active) {
       const u32x4* blk = &smem[u][lane];
+      const u32x4* wblk = &smem[u][0];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         u32x4 fa[4], fb[2];
 #pragma unroll
         for (int i = 0; i < 4; ++i) fa[i] = blk[((wm * 4 + i) * KS + ks) * 64];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) fb[j] = blk[(XT_BLK + (wn * 2 + j) * KS + ks) * 64];
+        for (int j = 0; j < 2; ++j) fb[j] = wblk[(XT_BLK + (wn * 2 + j) * KS + ks) * 64 + wslot(l32, 2 * ks + g)];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -267,7 +275,10 @@ __global__ void __launch_bounds__(512, 2) expand_tile_kernel(ExpandArgs a, int M
   uint16_t* stile = reinterpret_cast<uint16_t*>(&smem[0][0]) + wave * (16384 / 2);
   if (!COLS) {
     // C^T tiles: lane holds columns (r/4)*8 + 4g + r%4 of token l32; tile
-    // [128 tokens][8 chunks of 8 columns], chunk c of row r stored at c ^ (r & 7)
+    // [128 tokens][8 chunks of 8 columns], chunk c of row r stored at
+    // c ^ ((r >> 1) & 7): two 128-byte rows share a 256-byte bank window, so
+    // the 16 rows 0-15 of a store then cover all 16 chunk positions (with
+    // c ^ (r & 7) rows r and r+8 collide: a 4-way conflict)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -278,7 +289,7 @@ __global__ void __launch_bounds__(512, 2) expand_tile_kernel(ExpandArgs a, int M
           u32x2 o;
           o[0] = ET::pack2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
           o[1] = ET::pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-          *reinterpret_cast<u32x2*>(stile + row * 64 + ((chunk ^ (row & 7)) * 8) + 4 * g) = o;
+          *reinterpret_cast<u32x2*>(stile + row * 64 + ((chunk ^ ((row >> 1) & 7)) * 8) + 4 * g) = o;
         }
     // each lane then writes 8 columns (16 bytes) of one token: 8 tokens x
     // 128 contiguous bytes per store instruction
@@ -293,7 +304,7 @@ __global__ void __launch_bounds__(512, 2) expand_tile_kernel(ExpandArgs a, int M
         const size_t rowi = ((size_t)b * a.H + h) * a.Tcap + a.t_off + t;
         uint16_t* dst = (VPART ? a.v + rowi * a.Dv : a.k + rowi * a.k_ld) + cw + ch * 8;
         // nontemporal: the expanded rows are written once (about 3.8% faster)
-        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stile + tl * 64 + ((ch ^ (tl & 7)) * 8)),
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stile + tl * 64 + ((ch ^ ((tl >> 1) & 7)) * 8)),
                                     reinterpret_cast<u32x4*>(dst));
       }
       t += 8;
