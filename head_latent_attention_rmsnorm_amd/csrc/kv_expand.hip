@@ -166,12 +166,13 @@ __global__ void __launch_bounds__(512, 2) expand_tile_kernel(ExpandArgs a, int M
     wrow[j] = a.W + row * R + ((tid + 512 * j) % CPR) * 8;
   }
   // W fragment slots are XOR-permuted: slot (row r, 8-element chunk kc of
-  // the stage) sits at (r ^ 4kc) + 32(kc & 1) of its k-step's block. The four
-  // threads that load one row's four chunks then store to four different
-  // bank groups (without the permutation they hit the same one, a 4-way
-  // conflict), and an operand read (16 lanes, 16 consecutive rows, one
-  // chunk) still covers all 16 bank groups.
-  auto wslot = [](int r, int kc) __attribute__((always_inline)) { return (r ^ (4 * kc)) + 32 * (kc & 1); };
+  // the stage) sits at (r ^ X(kc)) + 32(kc & 1) of its k-step's block, with
+  // X = 0, 10, 4, 14. The 16 stores of a 16-lane group (rows 4q..4q+3, chunks
+  // 0..3) then land on 16 different bank groups, and so do the 8 of every
+  // 8-lane half (without the permutation the four chunks of a row hit one
+  // bank group, a 4-way conflict); an operand read (16 lanes, 16
+  // consecutive rows, one chunk) still covers all 16.
+  auto wslot = [](int r, int kc) __attribute__((always_inline)) { return (r ^ ((2 * kc) ^ (8 * (kc & 1)))) + 32 * (kc & 1); };
   // W chunks of the stages in flight are held in registers, one set per
   // stage buffer (the stage loop is unrolled by XT_NB so the set is static)
   u32x4 wreg[XT_NB][WPT];
