@@ -232,6 +232,23 @@ __global__ void __launch_bounds__(64) absorb_q_kernel(AbsorbArgs a) {
   const int rb = blockIdx.x, h = blockIdx.y, b0 = blockIdx.z * 32;
   const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
   const int Dqk = a.Dn + a.Dr;
+  // rotary query: lane (sequence b0 + l32, half g) of wave rb rotates pair
+  // 2*rb + g (the 16 waves of a head cover its Dr/2 = 32 pairs). Its loads
+  // (position, then table entries) go first, so that their latency overlaps
+  // the absorb product below; the results are stored after it.
+  const int rbq = b0 + l32, ri = 2 * rb + g, half = a.Dr >> 1;
+  const bool rot = rbq < a.B && ri < half;
+  const int ia = a.pairing ? 2 * ri : ri;
+  const int ib = a.pairing ? 2 * ri + 1 : ri + half;
+  float rc = 0.f, rs = 0.f, xa = 0.f, xb = 0.f;
+  if (rot) {
+    const int p = min(max(a.q_pos[rbq], 0), a.table_len - 1);
+    rc = a.cos[(size_t)p * half + ri];
+    rs = a.sin[(size_t)p * half + ri];
+    const uint16_t* qp = a.q + ((size_t)rbq * a.H + h) * Dqk + a.Dn;
+    xa = bf2f(qp[ia]);
+    xb = bf2f(qp[ib]);
+  }
   {
     const int b = b0 + l32;
     const uint16_t* qrow = a.q + ((size_t)min(b, a.B - 1) * a.H + h) * Dqk;
@@ -262,21 +279,10 @@ __global__ void __launch_bounds__(64) absorb_q_kernel(AbsorbArgs a) {
       if (bb < a.B) a.qa[((size_t)bb * a.H + h) * LW + rb * 32 + l32] = f2h(acc[i] * a.qscale);
     }
   }
-  {
-    // rotary query: lane (sequence b0 + l32, half g) of wave rb rotates pair
-    // 2*rb + g (the 16 waves of a head cover its Dr/2 = 32 pairs)
-    const int b = b0 + l32, i = 2 * rb + g, half = a.Dr >> 1;
-    if (b < a.B && i < half) {
-      const int p = min(max(a.q_pos[b], 0), a.table_len - 1);
-      const float c = a.cos[(size_t)p * half + i], sn = a.sin[(size_t)p * half + i];
-      const int ia = a.pairing ? 2 * i : i;
-      const int ib = a.pairing ? 2 * i + 1 : i + half;
-      const uint16_t* qp = a.q + ((size_t)b * a.H + h) * Dqk + a.Dn;
-      const float xa = bf2f(qp[ia]), xb = bf2f(qp[ib]);
-      uint16_t* dst = a.qa + ((size_t)b * a.H + h) * LW + LR;
-      dst[ia] = f2h((xa * c - xb * sn) * a.qscale);
-      dst[ib] = f2h((xb * c + xa * sn) * a.qscale);
-    }
+  if (rot) {
+    uint16_t* dst = a.qa + ((size_t)rbq * a.H + h) * LW + LR;
+    dst[ia] = f2h((xa * rc - xb * rs) * a.qscale);
+    dst[ib] = f2h((xb * rc + xa * rs) * a.qscale);
   }
 }
 
