@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmla.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["rope_table.hip", "rmsnorm.hip", "kv_expand.hip", "prefill_attn.hip", "decode_attn.hip", "decode_latent.hip",
+SOURCES = ["rope_table.hip", "rmsnorm.hip", "kv_expand.hip", "prefill_attn.hip", "prefill_dual.hip", "decode_attn.hip", "decode_latent.hip",
            "linear.hip", "ceiling.hip",
            "api.cpp"]
 

@@ -75,6 +75,9 @@ struct PrefillArgs {
 };
 bool prefill_supported(int Dqk, int Dr, int Dv);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// 192/128 heads, two 32-row query blocks per wave (prefill_dual.hip)
+bool prefill_dual_supported(int Dqk, int Dr, int Dv);
+hipError_t launch_prefill_dual(const PrefillArgs& a, hipStream_t stream);
 // row-major values [BH, T, Dv] -> V^T [BH, Dv, v_ld], columns T..v_ld-1 zero
 hipError_t launch_transpose_v(const uint16_t* v, uint16_t* vt, int BH, int T, int Dv, int v_ld, hipStream_t stream);
 

@@ -47,15 +47,14 @@
 //    the score MFMAs of sub-tile 1 are issued ahead of the softmax of
 //    sub-tile 0, and the PV MFMAs of sub-tile 0 ahead of the softmax of
 //    sub-tile 1;
-//  - MFMA and VALU work hardly overlap on this chip, so the softmax is cut to
-//    the bone: in fp16 mode the query is pre-scaled by scale*log2(e) and the
+//  - the softmax is cut to the bone: in fp16 mode the query is pre-scaled by scale*log2(e) and the
 //    first MFMA of every score chain accumulates onto -m (the running
 //    reference maximum), so the scores leave the MFMA as exp2 arguments
 //    (for 256-wide values, where registers rather than VALU issue are the
 //    limit, -m is subtracted on the VALU instead). The
 //    reference only moves when a sub-tile's P would leave a safe range: the
-//    per-lane sum of the sub-tile's P (taken anyway, with v_dot2 on the
-//    packed 16-bit P that the PV product consumes) bounds every P, and only
+//    per-lane sum of the sub-tile's P (taken anyway, in fp32 adds: a packed
+//    fp16 dot product does not co-issue with the MFMAs) bounds every P, and only
 //    when it exceeds 2^14 (or on the first sub-tile) is the exact maximum
 //    taken and the reference raised to it (exact: O and the row sum share
 //    the reference);
@@ -372,7 +371,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) prefill_kernel(PrefillArgs a, i
           const float p0 = __builtin_amdgcn_exp2f(sacc[j][8 * mm + 2 * e2]);
           const float p1 = __builtin_amdgcn_exp2f(sacc[j][8 * mm + 2 * e2 + 1]);
           pk[e2] = ET::pack2(p0, p1);
-          t = ET::sum2(pk[e2], t);
+          t += p0 + p1;  // fp32 adds: a packed dot product would not overlap the MFMAs
         }
         pf[2 * j + mm] = pk;
       }
@@ -557,7 +556,13 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  return a.kv_dtype == F16::code ? launch_prefill_t<F16>(a, stream) : launch_prefill_t<BF16>(a, stream);
+  // 192/128 heads over more than one round of 256-row work items: two row
+  // blocks per wave (prefill_dual.hip); a single round (short sequences)
+  // keeps the 8-wave kernel, whose paired 128-row blocks even out the causal
+  // work of the one round
+  if (prefill_dual_supported(a.Dn + a.Dr, a.Dr, a.Dv) && (int64_t)a.B * a.H * ((a.T + 255) / 256) > 256)
+    return launch_prefill_dual(a, stream);
+  return launch_prefill_t<F16>(a, stream);
 }
 
 }  // namespace mla

@@ -197,8 +197,10 @@ mla_status mla_kv_expand(const uint16_t* c_norm, const mla_bf16* W, int32_t B, i
  *   S = scale * Q K^T, keys s > t hidden (causal), P = softmax over s in fp32,
  *   out[b,h,t,:] = P V.
  * Flash-style: S and P are never written to memory. Both products run on
- * 16-bit MFMA in kv_dtype with fp32 accumulation: the rotated query and key
- * parts and P are rounded once to kv_dtype.
+ * fp16 MFMA with fp32 accumulation: the rotated query and key parts and P
+ * are rounded once to fp16. kv_dtype must be MLA_DTYPE_FP16: with bf16 keys,
+ * values and P the path's error reaches its 2e-2 bound (max-abs against the
+ * fp64 definition), so MLA_DTYPE_BF16 returns MLA_ERR_UNSUPPORTED.
  * Args: q device bf16 [B, H, T, Dn+Dr] (rotary part not rotated);
  *   k_nope device [B, H, T, Dn] and v device of element type kv_dtype (from
  *   mla_kv_expand), v either [B, H, T, Dv] (v_layout MLA_V_ROWS, v_ld
@@ -263,7 +265,8 @@ mla_status mla_rotate_rope_key(const mla_bf16* k_pe, const float* cos, const flo
  *   device fp32 [table_len, Dr/2]; out device bf16 [B, H, T, Dv]; lse device
  *   fp32 [B, H, T] or NULL. past >= 0, past + T <= Tcap; supported (Dn+Dr,
  *   Dv) as for mla_prefill_attention; one (b, h) slice of k_nope and of V^T
- *   below 2 GiB. No workspace.
+ *   below 2 GiB. No workspace. kv_dtype MLA_DTYPE_FP16 only, as for
+ *   mla_prefill_attention (MLA_ERR_UNSUPPORTED otherwise).
  * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED,
  *   MLA_ERR_ROPE_TYPE, MLA_ERR_HIP. */
 mla_status mla_prefill_attention_cached(const mla_bf16* q, const uint16_t* k_nope, const uint16_t* k_rot,

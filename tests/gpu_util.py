@@ -14,10 +14,6 @@ import workloads
 # rotated rotary parts and of P dominate).
 MAX_ABS = 2e-2
 REL_L2 = 5e-3
-# With bf16 (instead of fp16) intermediate keys/values the bf16 rounding of
-# k_nope, v and P adds up to about one more bf16 ulp of outputs in [2, 4)
-# (2^-6); the max-abs bound of that mode is widened by half of it.
-BF16_MAX_ABS = 3e-2
 
 
 def say(*a):
