@@ -34,8 +34,9 @@ EXPORTS = [
     "mla_rope_table_build", "mla_softmax_scale", "mla_latent_rmsnorm", "mla_kv_expand",
     "mla_prefill_attention", "mla_decode_attention", "mla_absorb_prepare", "mla_latent_cache_append",
     "mla_decode_absorbed", "mla_rotate_rope_key", "mla_prefill_attention_cached", "mla_decode_latent_expanded",
-    "mla_linear", "mla_rmsnorm", "mla_status_string",
+    "mla_linear", "mla_rmsnorm", "mla_decode_attention_noalloc", "mla_status_string",
 ]
+DECODE_SCRATCH_BYTES = 16 << 20  # MLA_DECODE_SCRATCH_BYTES
 # the measurement aids mla_ceiling.h declares
 CEILING_EXPORTS = ["mla_ceiling_hbm_read", "mla_ceiling_mfma", "mla_device_info"]
 CEILING_MFMA_OPERAND_BYTES = 49152
@@ -89,6 +90,8 @@ def load() -> ctypes.CDLL:
                                           I32, P, P, P, SZ, P]
     lib.mla_decode_attention.argtypes = [P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F32, I32, I32,
                                          P, SZ, P, P]
+    lib.mla_decode_attention_noalloc.argtypes = [P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F32,
+                                                 I32, I32, P, P]
     lib.mla_absorb_prepare.argtypes = [P, I32, I32, I32, I32, P, P]
     lib.mla_latent_cache_append.argtypes = [P, P, F32, P, P, P, I32, P, I32, I32, I32, I32, P, I32, P]
     lib.mla_decode_absorbed.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, F32, I32,

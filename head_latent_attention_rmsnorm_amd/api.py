@@ -19,7 +19,7 @@ __all__ = [
     "RopeParams", "rope_params", "mla_rope_table_build", "mla_softmax_scale", "mla_latent_rmsnorm",
     "mla_kv_expand", "mla_prefill_attention", "mla_decode_attention", "mla_absorb_prepare",
     "mla_latent_cache_append", "mla_decode_absorbed", "mla_rotate_rope_key", "mla_prefill_attention_cached",
-    "mla_decode_latent_expanded", "mla_linear", "mla_rmsnorm", "pairing_code",
+    "mla_decode_latent_expanded", "mla_linear", "mla_rmsnorm", "mla_decode_attention_noalloc", "pairing_code",
     "PAIR_HALF", "PAIR_INTERLEAVED", "ROPE_DEFAULT", "ROPE_YARN",
 ]
 
@@ -351,6 +351,43 @@ def mla_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
 
 
 # ---- decode against a compressed-latent cache (absorbed form)
+
+
+def mla_decode_attention_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                 seq_len: torch.Tensor, q_pos: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor,
+                                 scale: float, Dn: int, pairing="half", num_splits: int = 0,
+                                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mla_decode_attention without a workspace: the split partials live in
+    the library's static per-GPU scratch (MLA_DECODE_SCRATCH_BYTES). Give
+    `out` to allocate nothing at all."""
+    _need(q, "q")
+    code = _kv_code(k_cache, "k_cache")
+    _need(k_cache, "k_cache", k_cache.dtype)
+    _need(v_cache, "v_cache", k_cache.dtype)
+    _need(seq_len, "seq_len", torch.int32)
+    _need(q_pos, "q_pos", torch.int32)
+    _need(cos, "cos", torch.float32)
+    _need(sin, "sin", torch.float32)
+    B, H, Tcap, Dqk = k_cache.shape
+    Dv = v_cache.shape[-1]
+    Dr = Dqk - Dn
+    _shape(q, "q", (B, H, 1, Dqk))
+    _shape(v_cache, "v_cache", (B, H, Tcap, Dv))
+    _shape(seq_len, "seq_len", (B,))
+    _shape(q_pos, "q_pos", (B,))
+    _shape(sin, "sin", cos.shape)
+    if cos.dim() != 2 or cos.shape[1] != Dr // 2:
+        raise ValueError(f"cos should be [table_len, {Dr // 2}], but is {tuple(cos.shape)}")
+    if out is None:
+        out = torch.empty((B, H, 1, Dv), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out")
+    _shape(out, "out", (B, H, 1, Dv))
+    check("mla_decode_attention_noalloc",
+          _lib.load().mla_decode_attention_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), code, _ptr(seq_len),
+                                                   _ptr(q_pos), _ptr(cos), _ptr(sin), cos.shape[0], B, H, Tcap, Dn,
+                                                   Dr, Dv, float(scale), pairing_code(pairing), int(num_splits),
+                                                   _ptr(out), _stream(q)))
+    return out
 
 def mla_absorb_prepare(W: torch.Tensor, H: int, Dn: int, Dv: int,
                        out: Optional[torch.Tensor] = None) -> torch.Tensor:

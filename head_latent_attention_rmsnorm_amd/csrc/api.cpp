@@ -279,38 +279,93 @@ mla_status mla_prefill_attention_cached(const mla_bf16* q, const uint16_t* k_nop
   return hip_status(mla::launch_prefill(a, stream));
 }
 
-mla_status mla_decode_attention(const mla_bf16* q, const uint16_t* k_cache, const uint16_t* v_cache,
-                                int32_t cache_dtype, const int32_t* seq_len, const int32_t* q_pos, const float* cos, const float* sin,
-                                int32_t table_len, int32_t B, int32_t H, int32_t Tcap, int32_t Dn, int32_t Dr,
-                                int32_t Dv, float scale, int32_t pairing, int32_t num_splits, void* workspace,
-                                size_t* ws_bytes, mla_bf16* out, hipStream_t stream) {
+namespace {
+// Argument checks shared by the two decode entry points; on MLA_OK, *S and
+// *need hold the split count and the bytes of split partials it needs.
+mla_status decode_check(const mla_bf16* q, const uint16_t* k_cache, const uint16_t* v_cache, int32_t cache_dtype,
+                        const int32_t* seq_len, const int32_t* q_pos, const float* cos, const float* sin,
+                        int32_t table_len, int32_t B, int32_t H, int32_t Tcap, int32_t Dn, int32_t Dr, int32_t Dv,
+                        float scale, int32_t pairing, int32_t num_splits, const mla_bf16* out, int* S,
+                        size_t* need, bool* query_only, bool ws_query) {
+  *query_only = false;
   if (B < 0 || H < 1 || Tcap < 1 || Dn < 1 || Dr < 2 || (Dr & 1) || Dv < 1) return MLA_ERR_SHAPE;
   if (!mla::decode_supported(Dn + Dr, Dv) || !dtype_ok(cache_dtype)) return MLA_ERR_UNSUPPORTED;
   if (!pairing_ok(pairing)) return MLA_ERR_ROPE_TYPE;
   if (num_splits < 0 || num_splits > 256 || num_splits > Tcap) return MLA_ERR_SHAPE;
   if ((int64_t)B * H * Tcap * (Dn + Dr) > kMaxElems || B > 65535 || H > 65535) return MLA_ERR_SHAPE;
-  const int S = num_splits ? num_splits : mla::decode_auto_splits(B, H, Tcap);
-  const size_t need = mla::decode_workspace_bytes(B, H, Dv, S);
-  if (!workspace && ws_bytes) {
-    *ws_bytes = need;
+  *S = num_splits ? num_splits : mla::decode_auto_splits(B, H, Tcap);
+  *need = mla::decode_workspace_bytes(B, H, Dv, *S);
+  if (ws_query) {
+    *query_only = true;
     return MLA_OK;
   }
   if (!(scale > 0.0f) || !isfinite(scale)) return MLA_ERR_SHAPE;
   if (B == 0) return MLA_OK;
   if (!q || !k_cache || !v_cache || !seq_len || !q_pos || !cos || !sin || !out) return MLA_ERR_NULL;
   if (table_len < 1) return MLA_ERR_SHAPE;
-  if (need > 0 && (!workspace || (ws_bytes && *ws_bytes < need))) return MLA_ERR_WORKSPACE;
-  if (!aligned16(k_cache) || !aligned16(v_cache) || (need > 0 && !aligned16(workspace))) return MLA_ERR_SHAPE;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
+mla_status decode_launch(const mla_bf16* q, const uint16_t* k_cache, const uint16_t* v_cache, int32_t cache_dtype,
+                         const int32_t* seq_len, const int32_t* q_pos, const float* cos, const float* sin,
+                         int32_t table_len, int32_t B, int32_t H, int32_t Tcap, int32_t Dn, int32_t Dr, int32_t Dv,
+                         float scale, int32_t pairing, int S, size_t need, void* workspace, mla_bf16* out,
+                         hipStream_t stream) {
   float* part_o = static_cast<float*>(workspace);
   float* part_ml = nullptr;
   if (need > 0) {
     const size_t n = (size_t)B * H * S;
     part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((n * Dv * sizeof(float)) + 255) / 256 * 256);
   }
-  clear_stale_error();
   mla::DecodeArgs a{q, k_cache, v_cache, seq_len, q_pos, cos, sin, table_len, B, H, Tcap, Dn, Dr, Dv, pairing, S,
                     scale, part_o, part_ml, out, cache_dtype};
   return hip_status(mla::launch_decode(a, stream));
+}
+}  // namespace
+
+mla_status mla_decode_attention(const mla_bf16* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                int32_t cache_dtype, const int32_t* seq_len, const int32_t* q_pos, const float* cos,
+                                const float* sin, int32_t table_len, int32_t B, int32_t H, int32_t Tcap, int32_t Dn,
+                                int32_t Dr, int32_t Dv, float scale, int32_t pairing, int32_t num_splits,
+                                void* workspace, size_t* ws_bytes, mla_bf16* out, hipStream_t stream) {
+  int S = 0;
+  size_t need = 0;
+  bool query_only = false;
+  mla_status st = decode_check(q, k_cache, v_cache, cache_dtype, seq_len, q_pos, cos, sin, table_len, B, H, Tcap, Dn,
+                               Dr, Dv, scale, pairing, num_splits, out, &S, &need, &query_only,
+                               !workspace && ws_bytes);
+  if (st != MLA_OK) return st;
+  if (query_only) {
+    *ws_bytes = need;
+    return MLA_OK;
+  }
+  if (B == 0) return MLA_OK;
+  if (need > 0 && (!workspace || (ws_bytes && *ws_bytes < need))) return MLA_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return MLA_ERR_SHAPE;
+  clear_stale_error();
+  return decode_launch(q, k_cache, v_cache, cache_dtype, seq_len, q_pos, cos, sin, table_len, B, H, Tcap, Dn, Dr, Dv,
+                       scale, pairing, S, need, workspace, out, stream);
+}
+
+mla_status mla_decode_attention_noalloc(const mla_bf16* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                        int32_t cache_dtype, const int32_t* seq_len, const int32_t* q_pos,
+                                        const float* cos, const float* sin, int32_t table_len, int32_t B, int32_t H,
+                                        int32_t Tcap, int32_t Dn, int32_t Dr, int32_t Dv, float scale,
+                                        int32_t pairing, int32_t num_splits, mla_bf16* out, hipStream_t stream) {
+  int S = 0;
+  size_t need = 0;
+  bool query_only = false;
+  mla_status st = decode_check(q, k_cache, v_cache, cache_dtype, seq_len, q_pos, cos, sin, table_len, B, H, Tcap, Dn,
+                               Dr, Dv, scale, pairing, num_splits, out, &S, &need, &query_only, false);
+  if (st != MLA_OK) return st;
+  if (B == 0) return MLA_OK;
+  if (need > mla::kDecodeScratchBytes) return MLA_ERR_WORKSPACE;  // split partials beyond the static scratch
+  void* ws = nullptr;
+  clear_stale_error();
+  if (need > 0 && mla::decode_scratch(&ws) != hipSuccess) return MLA_ERR_HIP;
+  return decode_launch(q, k_cache, v_cache, cache_dtype, seq_len, q_pos, cos, sin, table_len, B, H, Tcap, Dn, Dr, Dv,
+                       scale, pairing, S, need, ws, out, stream);
 }
 
 // ---- decode against a compressed-latent cache (absorbed form)

@@ -16,6 +16,8 @@
 // about 7 TB/s.
 // A split writes (max, sum, unnormalised output) and a combine kernel merges
 // the splits with the log-sum-exp rule; a single split writes the output.
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -286,6 +288,35 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.H), dim3(128), 0, stream, a.part_o, a.part_ml,
                      a.num_splits, a.Dv, a.out);
   return hipGetLastError();
+}
+
+// Scratch of the allocation-free decode entry point: the split partials
+// (o [B, H, S, Dv], then (m, l) [B, H, S, 2], as in a caller's workspace)
+// live in this array, one copy per GPU, held until the process ends. Every
+// split writes all of its partials and the combine reads only those, so
+// nothing here needs clearing between calls; calls that overlap on one GPU
+// race on it.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* dev_ptr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!dev_ptr[dev]) {
+    // the array's device address on this (current) device; the host-side
+    // name is only a stand-in and must never reach a kernel
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    dev_ptr[dev] = p;
+  }
+  *ptr = dev_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace mla

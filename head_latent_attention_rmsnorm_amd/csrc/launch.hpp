@@ -101,6 +101,10 @@ bool decode_supported(int Dqk, int Dv);
 int decode_auto_splits(int B, int H, int Tcap);
 size_t decode_workspace_bytes(int B, int H, int Dv, int splits);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// the allocation-free decode entry point's scratch: its size, and its device
+// address on the current device (looked up once per device)
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+hipError_t decode_scratch(void** ptr);
 
 // ---- decode against a compressed-latent cache (absorbed form); the cache
 // row is 576 fp16 values: 512 latent then 64 rotated rotary key

@@ -303,6 +303,27 @@ mla_status mla_decode_attention(const mla_bf16* q, const uint16_t* k_cache,
                                 int32_t num_splits, void* workspace, size_t* ws_bytes,
                                 mla_bf16* out, hipStream_t stream);
 
+/* Decode attention that allocates nothing, for callers that cannot allocate
+ * or bring a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments, outputs and errors as
+ * mla_decode_attention without workspace/ws_bytes: the split partials
+ * (B*H*S*(Dv+2)*4 bytes, 256-byte aligned, when S > 1) go to a static device
+ * array of MLA_DECODE_SCRATCH_BYTES (16 MiB) inside the library instead, one
+ * per GPU, held until the process ends. A call whose partials would exceed
+ * it returns MLA_ERR_WORKSPACE and queues nothing (choose fewer splits, or
+ * use mla_decode_attention). Calls that overlap on one GPU (different
+ * streams or host threads) share that array and race: serialise them. The
+ * array's device address is looked up on the first call on each device
+ * (MLA_ERR_HIP if that fails). */
+#define MLA_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+mla_status mla_decode_attention_noalloc(const mla_bf16* q, const uint16_t* k_cache,
+                                        const uint16_t* v_cache, int32_t cache_dtype,
+                                        const int32_t* seq_len, const int32_t* q_pos,
+                                        const float* cos, const float* sin, int32_t table_len,
+                                        int32_t B, int32_t H, int32_t Tcap, int32_t Dn, int32_t Dr,
+                                        int32_t Dv, float scale, int32_t pairing,
+                                        int32_t num_splits, mla_bf16* out, hipStream_t stream);
+
 /* ---- Decode against a compressed-latent cache ---------------------------
  * Cache layout (the "latent cache"): device fp16 [B, Lcap, R+Dr], row s of
  * sequence b = [ normalised latent of token s (R values) | its rotary key

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared()
-    assert len(names) == 15
+    assert len(names) == 16
     assert sorted(_lib.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -167,6 +167,40 @@ def test_decode_validation(lib):
     assert decode(lib, dtype=3) == UNSUP
     assert decode(lib, B=0) == OK
     assert decode(lib, B=0, splits=0) == OK  # automatic split count of an empty batch
+
+
+def decode_noalloc(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, dtype=0, seq=FAKE, qpos=FAKE, cos=FAKE, sin=FAKE, table_len=1001, B=32, H=64,
+             Tcap=1001, Dn=128, Dr=64, Dv=128, scale=0.13, pairing=0, splits=0, out=FAKE)
+    a.update(kw)
+    return lib.mla_decode_attention_noalloc(a["q"], a["kc"], a["vc"], a["dtype"], a["seq"], a["qpos"], a["cos"],
+                                            a["sin"], a["table_len"], a["B"], a["H"], a["Tcap"], a["Dn"], a["Dr"],
+                                            a["Dv"], ctypes.c_float(a["scale"]), a["pairing"], a["splits"], a["out"],
+                                            None)
+
+
+def test_decode_noalloc_validation(lib):
+    """Rejections happen on the host before any HIP call: the same argument
+    checks as the workspace entry point, and split partials beyond the static
+    scratch (B*H*S*(Dv+2)*4 bytes > 16 MiB) are refused with
+    MLA_ERR_WORKSPACE."""
+    assert _lib.DECODE_SCRATCH_BYTES == 16 << 20
+    assert re.search(r"#define MLA_DECODE_SCRATCH_BYTES \(\(size_t\)16 << 20\)", open(HEADER).read())
+    assert decode_noalloc(lib, kc=None) == NULL
+    assert decode_noalloc(lib, out=None) == NULL
+    assert decode_noalloc(lib, Dn=96) == UNSUP
+    assert decode_noalloc(lib, dtype=3) == UNSUP
+    assert decode_noalloc(lib, pairing=-1) == ROPE
+    assert decode_noalloc(lib, splits=-2) == SHAPE
+    assert decode_noalloc(lib, splits=300) == SHAPE
+    assert decode_noalloc(lib, scale=0.0) == SHAPE
+    assert decode_noalloc(lib, table_len=0) == SHAPE
+    assert decode_noalloc(lib, B=0) == OK
+    # 32 x 64 x 8 splits: 32*64*8*130*4 = 8.5 MB fits; 16 splits (17 MB) and
+    # 256 sequences x 64 heads x 4 splits (34 MB) do not
+    assert 32 * 64 * 16 * (128 + 2) * 4 > _lib.DECODE_SCRATCH_BYTES
+    assert decode_noalloc(lib, splits=16) == WS
+    assert decode_noalloc(lib, B=256, splits=4) == WS
 
 
 def test_absorb_prepare_validation(lib):
