@@ -135,8 +135,11 @@ __global__ void __launch_bounds__(512, 2) expand_tile_kernel(ExpandArgs a, int M
 
   // latent: LDS-direct loads, APW blocks per wave per stage; block bi =
   // (m-tile bi/KS, k-step bi%KS), lane = (row l32, 8 columns at 8g); rows
-  // past the last token read as zeros
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.c + (size_t)m0 * R, (uint32_t)(M - m0) * (uint32_t)R * 2u);
+  // past the last token read as zeros. The descriptor covers this tile's
+  // rows only (at most XT_M * R * 2 bytes), so its 32-bit range never wraps
+  // however many tokens the call has.
+  const uint32_t rows = (uint32_t)min(M - m0, XT_M);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.c + (size_t)m0 * R, rows * (uint32_t)R * 2u);
   uint32_t voff[APW];
 #pragma unroll
   for (int i = 0; i < APW; ++i) {
