@@ -1,7 +1,9 @@
 // cos/sin table builder (Kimi-K2 "RoPE coefficients", section "Generate RoPE
-// coefficients": frequency blend by the YaRN linear ramp, outer product with
-// the positions, sin/cos scaled by the mscale ratio). One thread per
-// (position, pair); the ramp, frequencies and angles are fp32 as on the page.
+// coefficients": under YaRN each pair's frequency moves from base^(-2i/Dr)
+// towards base^(-2i/Dr)/factor by the linear ramp's fraction r_i over the
+// correction band; angles p * frequency; sin/cos scaled by the mscale
+// ratio). One thread per (position, pair); ramp, frequencies and angles in
+// fp32, as the page computes them.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -17,14 +19,13 @@ __global__ void __launch_bounds__(256) rope_table_kernel(RopeResolved r, int n_p
   // exponent 2i/dim, as arange(0, dim, 2) / dim in fp32
   const float e = (float)(2 * i) / (float)r.dim;
   const float powb = powf(r.base, e);
-  const float extra = 1.0f / powb;  // unscaled frequency
-  float inv = extra;
+  const float theta = 1.0f / powb;  // unscaled frequency
+  float inv = theta;
   if (r.yarn) {
-    const float inter = 1.0f / (r.factor * powb);  // interpolated frequency
-    float ramp = ((float)i - r.low) / (r.high - r.low);
-    ramp = fminf(fmaxf(ramp, 0.0f), 1.0f);
-    const float keep = 1.0f - ramp;  // weight of the unscaled frequency
-    inv = inter * (1.0f - keep) + extra * keep;
+    // fraction of the way to the interpolated frequency theta / factor:
+    // 0 below the band, 1 above it, linear across it
+    const float frac = fminf(fmaxf(((float)i - r.low) / (r.high - r.low), 0.0f), 1.0f);
+    inv = theta + (1.0f / (r.factor * powb) - theta) * frac;
   }
   const float ang = (float)p * inv;
   float s, c;

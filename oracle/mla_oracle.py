@@ -90,21 +90,20 @@ def rope_base_freqs(base: float, dim: int) -> np.ndarray:
 def rope_inv_freq(spec, dim: int) -> np.ndarray:
     """Per-pair angular frequency [dim/2].
 
-    Default RoPE: theta_i. YaRN [K2-rope, _set_cos_sin_cache]: the extrapolated
-    frequency theta_i and the interpolated theta_i/factor are blended by
-    mask = 1 - ramp(low, high): pairs below the band keep theta_i, pairs
-    above it take theta_i/factor."""
+    Default RoPE: theta_i. YaRN [K2-rope, _set_cos_sin_cache]: each pair's
+    frequency moves from the unscaled theta_i towards the interpolated
+    theta_i/factor by the fraction r_i = ramp(low, high) of the way:
+    theta_i + (theta_i/factor - theta_i) * r_i. Pairs below the band
+    (r = 0) keep theta_i, pairs above it (r = 1) take theta_i/factor."""
     theta = rope_base_freqs(spec.base, dim)
     if spec.kind == "default":
         return theta
     if spec.kind != "yarn":
         raise ValueError(f"Unknown RoPE scaling type {spec.kind}")
-    freq_extra = theta
-    freq_inter = theta / spec.factor
     low, high = yarn_correction_range(spec.beta_fast, spec.beta_slow, dim, spec.base,
                                       spec.original_max_pos)
-    mask = 1.0 - yarn_linear_ramp(low, high, dim // 2)
-    return freq_inter * (1.0 - mask) + freq_extra * mask
+    r = yarn_linear_ramp(low, high, dim // 2)
+    return theta + (theta / spec.factor - theta) * r
 
 
 def rope_table_mscale(spec) -> float:
