@@ -1,8 +1,10 @@
 """Benchmark of the eager latent-attention forward path on one MI355X.
 
-One step = one pass of the whole hot path:
+One step = one pass of the whole hot path (the cos/sin tables are built once
+per length before the steps, as the pages cache them):
   prefill (Kimi-K2 shape, B=2, T=8192, H=64, Dn/Dr/Dv 128/64/128, YaRN):
-    cos/sin table -> latent RMSNorm -> kv_b_proj expansion -> causal attention
+    latent RMSNorm with the shared rotary key's rotation -> kv_b_proj
+    expansion -> causal attention;
   decode (Kimi-K2 shape, B=32 sequences at position 1000, 1001 cached rows):
     latent RMSNorm -> kv_b_proj expansion appended into the expanded cache ->
     split-K decode attention;
@@ -13,8 +15,9 @@ Inputs are drawn on the GPU (same seeded recipe as the parity tests) and are
 resident in HBM before the timed region starts.
 
 Reported (one JSON line):
-  value           prefill-path TFLOP/s (causal attention + kv_b_proj flops over
-                  the measured prefill time of a step)
+  value           prefill attention TFLOP/s (causal-pair flops over the mean
+                  event-timed attention launch of a step); the whole prefill
+                  path (attention + kv_b_proj flops) is config.prefill_path_*
   roofline        prefill attention kernel: algorithmic flops per launch over
                   its mean launch time (HIP events on the launch stream)
                   against the MI355X dense 16-bit MFMA peak
@@ -131,7 +134,8 @@ def cpu_baseline(budget_s: float) -> dict:
             break
     dt = time.perf_counter() - t0
     flops = heads * (attn_flops(wh) + expand_flops(wh))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "host_cpus": os.cpu_count(),
+            "kind": "oracle",
             "sample": f"{heads} head(s) of sequence 0 of {PREFILL} (T=8192): fp64 expansion + causal "
                       f"attention over all rows, {dt:.1f} s"}
 
@@ -193,20 +197,24 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     rec = {"prefill": [], "attn": [], "decode": [], "dec_attn": [], "lat": [], "lat_attn": []}
 
+    # cos/sin tables: built once per length, as the pages cache them
+    tab = mla.pipeline.build_table(rope_p, wp.T, wp.Dqk, dev)
+    tdec = mla.pipeline.build_table(rope_d, wd.cache_len, wd.Dqk, dev)
+    tlat = mla.pipeline.build_table(rope_l, wl.cache_len, wl.Dqk, dev)
+
     def step(timed: bool):
         e = [ev() for _ in range(8)] if timed else None
         if timed:
             e[0].record()
-        tab = mla.pipeline.build_table(rope_p, wp.T, wp.Dqk, dev)
-        mla.api.mla_latent_rmsnorm(ip["latent"], ip["gain"], wp.eps, out=bufs.c_norm)
+        mla.api.mla_latent_prepare(ip["latent"], ip["gain"], wp.eps, ip["k_pe"], tab.cos, tab.sin, wp.pairing,
+                                   c_norm=bufs.c_norm, k_rot=bufs.k_rot)
         mla.api.mla_kv_expand(bufs.c_norm, ip["W"], wp.H, wp.Dn, wp.Dv, k=bufs.k_nope, v=bufs.v, v_layout="cols")
         if timed:
             e[1].record()
-        mla.api.mla_prefill_attention(ip["q"], bufs.k_nope, ip["k_pe"], bufs.v, tab.cos, tab.sin, tab.scale,
-                                      wp.pairing, out=bufs.out, workspace=bufs.workspace, v_layout="cols")
+        mla.api.mla_prefill_attention_cached(ip["q"], bufs.k_nope, bufs.k_rot, bufs.v, 0, tab.cos, tab.sin,
+                                             tab.scale, wp.pairing, out=bufs.out)
         if timed:
             e[2].record()
-        tdec = mla.pipeline.build_table(rope_d, wd.cache_len, wd.Dqk, dev)
         mla.api.mla_latent_rmsnorm(idc["latent"], idc["gain"], wd.eps, out=c_dec)
         mla.api.mla_kv_expand(c_dec, idc["W"], wd.H, wd.Dn, wd.Dv, k=idc["k_cache"], v=idc["v_cache"],
                               t_off=wd.q_pos, k_pe=idc["k_pe"], cos=tdec.cos, sin=tdec.sin, pos=qpos.view(-1, 1),
@@ -217,7 +225,6 @@ def main():
                                      tdec.scale, wd.Dn, wd.pairing, splits, out=out_dec, workspace=ws_dec)
         if timed:
             e[4].record()
-        tlat = mla.pipeline.build_table(rope_l, wl.cache_len, wl.Dqk, dev)
         mla.api.mla_latent_cache_append(il["latent"].view(wl.B, wl.R), il["gain"], il["k_pe"].view(wl.B, wl.Dr),
                                         tlat.cos, tlat.sin, qpos_l, il["latent_cache"], wl.eps, wl.pairing)
         if timed:
@@ -253,11 +260,10 @@ def main():
     # chunk's own rows included), then time the chunk's attention call
     TQ = 1024
     past = wp.T - TQ
-    tab = mla.pipeline.build_table(rope_p, wp.T, wp.Dqk, dev)
-    mla.api.mla_latent_rmsnorm(ip["latent"], ip["gain"], wp.eps, out=bufs.c_norm)
+    mla.api.mla_latent_prepare(ip["latent"], ip["gain"], wp.eps, ip["k_pe"], tab.cos, tab.sin, wp.pairing,
+                               c_norm=bufs.c_norm, k_rot=bufs.k_rot)
     mla.api.mla_kv_expand(bufs.c_norm, ip["W"], wp.H, wp.Dn, wp.Dv, k=bufs.k_nope, v=bufs.v, v_layout="cols")
-    k_rot = torch.empty((wp.B, wp.T, wp.Dr), dtype=torch.float16, device=dev)
-    mla.api.mla_rotate_rope_key(ip["k_pe"], tab.cos, tab.sin, k_rot, 0, wp.pairing)
+    k_rot = bufs.k_rot
     q_chunk = ip["q"][:, :, past:].contiguous()
     out_chunk = torch.empty((wp.B, wp.H, TQ, wp.Dv), dtype=torch.bfloat16, device=dev)
 
@@ -278,7 +284,6 @@ def main():
 
     # latent-cache decode by re-expansion of every cached row (the eager
     # alternative to the absorbed form), attention call only
-    tlat = mla.pipeline.build_table(rope_l, wl.cache_len, wl.Dqk, dev)
     ws_rx = torch.empty((1400 << 20,), dtype=torch.uint8, device=dev)
 
     def reexpand():
@@ -341,12 +346,13 @@ def main():
         inp = workloads.make_inputs(w, device=dev)
         b = mla.pipeline.alloc_prefill(w.B, w.T, w.H, w.R, w.Dn, w.Dr, w.Dv, dev)
         t = mla.pipeline.build_table(mla.api.params_from(w.rope, w.Dr), w.T, w.Dqk, dev)
-        mla.api.mla_latent_rmsnorm(inp["latent"], inp["gain"], w.eps, out=b.c_norm)
+        mla.api.mla_latent_prepare(inp["latent"], inp["gain"], w.eps, inp["k_pe"], t.cos, t.sin, w.pairing,
+                                   c_norm=b.c_norm, k_rot=b.k_rot)
         mla.api.mla_kv_expand(b.c_norm, inp["W"], w.H, w.Dn, w.Dv, k=b.k_nope, v=b.v, v_layout="cols")
 
         def attn(w=w, inp=inp, b=b, t=t):
-            mla.api.mla_prefill_attention(inp["q"], b.k_nope, inp["k_pe"], b.v, t.cos, t.sin, t.scale, w.pairing,
-                                          out=b.out, workspace=b.workspace, v_layout="cols")
+            mla.api.mla_prefill_attention_cached(inp["q"], b.k_nope, b.k_rot, b.v, 0, t.cos, t.sin, t.scale,
+                                                 w.pairing, out=b.out)
         rec_s = {"warm_ms": median(launch_times(attn, 20))}
         if name == "kimi_k2_1k":
             flush = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
@@ -370,8 +376,9 @@ def main():
 
     # the two decode steps recorded once as HIP graphs and replayed (the same
     # calls as in the timed steps, table build included): launch-bound steps
+    td, tl = tdec, tlat
+
     def dec_step():
-        td = mla.pipeline.build_table(rope_d, wd.cache_len, wd.Dqk, dev)
         mla.api.mla_latent_rmsnorm(idc["latent"], idc["gain"], wd.eps, out=c_dec)
         mla.api.mla_kv_expand(c_dec, idc["W"], wd.H, wd.Dn, wd.Dv, k=idc["k_cache"], v=idc["v_cache"],
                               t_off=wd.q_pos, k_pe=idc["k_pe"], cos=td.cos, sin=td.sin, pos=qpos.view(-1, 1),
@@ -380,7 +387,6 @@ def main():
                                             td.scale, wd.Dn, wd.pairing, splits, out=out_dec, workspace=ws_dec)
 
     def lat_step():
-        tl = mla.pipeline.build_table(rope_l, wl.cache_len, wl.Dqk, dev)
         mla.api.mla_latent_cache_append(il["latent"].view(wl.B, wl.R), il["gain"], il["k_pe"].view(wl.B, wl.Dr),
                                         tl.cos, tl.sin, qpos_l, il["latent_cache"], wl.eps, wl.pairing)
         return mla.api.mla_decode_absorbed(il["q"], il["W"], w_ukt, il["latent_cache"], seq_l, qpos_l, tl.cos,
@@ -429,10 +435,11 @@ def main():
     t_lat_attn = mean(rec["lat_attn"]) * 1e-3
     lat_bytes = wl.B * wl.cache_len * (wl.R + wl.Dr) * 2  # the latent cache rows read
     fa, fe = attn_flops(wp), expand_flops(wp)
-    value = (fa + fe) / t_prefill / 1e12
+    path_tflops = (fa + fe) / t_prefill / 1e12
     attn_tflops = fa / t_attn / 1e12
+    value = attn_tflops  # the metric: prefill attention TFLOP/s
     dec_gbs = decode_bytes(wd) / t_dec_attn / 1e9
-    log(f"[bench] prefill path {t_prefill * 1e3:.3f} ms ({value:.1f} TFLOP/s), attention {t_attn * 1e3:.3f} ms "
+    log(f"[bench] prefill path {t_prefill * 1e3:.3f} ms ({path_tflops:.1f} TFLOP/s), attention {t_attn * 1e3:.3f} ms "
         f"({attn_tflops:.1f} TFLOP/s, {attn_tflops / MFMA_PEAK_TFLOPS:.1%} of peak); decode step "
         f"{t_decode * 1e6:.1f} us, decode attention {t_dec_attn * 1e6:.1f} us ({dec_gbs:.0f} GB/s); latent-cache "
         f"decode step {t_lat * 1e6:.1f} us (attention {t_lat_attn * 1e6:.1f} us); chunked prefill (1024 after "
@@ -467,6 +474,7 @@ def main():
             "prefill_attention_tflops": round(attn_tflops, 2),
             "prefill_attention_ms": round(t_attn * 1e3, 4),
             "prefill_path_ms": round(t_prefill * 1e3, 4),
+            "prefill_path_tflops": round(path_tflops, 2),
             "prefill_tokens_per_s": round(wp.B * wp.T / t_prefill, 1),
             "decode_attention_us": round(t_dec_attn * 1e6, 2),
             "decode_attention_gbs": round(dec_gbs, 1),
@@ -508,13 +516,13 @@ def main():
                 "head_latent_attention_rmsnorm_amd/csrc/decode_latent.hip", "decode_latent"),
         },
         "roofline": {
-            "kernel": "prefill_kernel (causal flash attention, Dqk 192, Dv 128)",
+            "kernel": "prefill_dual_kernel (causal flash attention, Dqk 192, Dv 128, two row blocks per wave)",
             "bound": "mfma",
             "achieved": round(attn_tflops, 2),
             "peak": MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / MFMA_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic("head_latent_attention_rmsnorm_amd/csrc/prefill_attn.hip"),
+            "traffic": measured_traffic("head_latent_attention_rmsnorm_amd/csrc/prefill_dual.hip", "prefill"),
         },
     }
     if not args.no_cpu_baseline:

@@ -34,7 +34,7 @@ EXPORTS = [
     "mla_rope_table_build", "mla_softmax_scale", "mla_latent_rmsnorm", "mla_kv_expand",
     "mla_prefill_attention", "mla_decode_attention", "mla_absorb_prepare", "mla_latent_cache_append",
     "mla_decode_absorbed", "mla_rotate_rope_key", "mla_prefill_attention_cached", "mla_decode_latent_expanded",
-    "mla_linear", "mla_rmsnorm", "mla_decode_attention_noalloc", "mla_status_string",
+    "mla_linear", "mla_rmsnorm", "mla_decode_attention_noalloc", "mla_latent_prepare", "mla_status_string",
 ]
 DECODE_SCRATCH_BYTES = 16 << 20  # MLA_DECODE_SCRATCH_BYTES
 # the measurement aids mla_ceiling.h declares
@@ -92,6 +92,7 @@ def load() -> ctypes.CDLL:
                                          P, SZ, P, P]
     lib.mla_decode_attention_noalloc.argtypes = [P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F32,
                                                  I32, I32, P, P]
+    lib.mla_latent_prepare.argtypes = [P, P, F32, P, P, P, I32, P, I32, I32, I32, I32, I32, P, P, P]
     lib.mla_absorb_prepare.argtypes = [P, I32, I32, I32, I32, P, P]
     lib.mla_latent_cache_append.argtypes = [P, P, F32, P, P, P, I32, P, I32, I32, I32, I32, P, I32, P]
     lib.mla_decode_absorbed.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, F32, I32,

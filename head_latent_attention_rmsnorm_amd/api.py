@@ -19,7 +19,8 @@ __all__ = [
     "RopeParams", "rope_params", "mla_rope_table_build", "mla_softmax_scale", "mla_latent_rmsnorm",
     "mla_kv_expand", "mla_prefill_attention", "mla_decode_attention", "mla_absorb_prepare",
     "mla_latent_cache_append", "mla_decode_absorbed", "mla_rotate_rope_key", "mla_prefill_attention_cached",
-    "mla_decode_latent_expanded", "mla_linear", "mla_rmsnorm", "mla_decode_attention_noalloc", "pairing_code",
+    "mla_decode_latent_expanded", "mla_linear", "mla_rmsnorm", "mla_decode_attention_noalloc", "mla_latent_prepare",
+    "pairing_code",
     "PAIR_HALF", "PAIR_INTERLEAVED", "ROPE_DEFAULT", "ROPE_YARN",
 ]
 
@@ -116,6 +117,42 @@ def mla_latent_rmsnorm(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
     check("mla_latent_rmsnorm",
           _lib.load().mla_latent_rmsnorm(_ptr(x), _ptr(w), float(eps), _ptr(y), n, R, _stream(x)))
     return y
+
+
+def mla_latent_prepare(latent: torch.Tensor, gain: torch.Tensor, eps: float, k_pe: torch.Tensor, cos: torch.Tensor,
+                       sin: torch.Tensor, pairing="half", pos: Optional[torch.Tensor] = None,
+                       c_norm: Optional[torch.Tensor] = None,
+                       k_rot: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Latent RMSNorm (latent bf16 [B, T, R] -> c_norm fp16) and the rotated
+    shared rotary key (k_pe bf16 [B, T, Dr] -> k_rot fp16) in one launch."""
+    _need(latent, "latent")
+    _need(gain, "gain")
+    _need(k_pe, "k_pe")
+    _need(cos, "cos", torch.float32)
+    _need(sin, "sin", torch.float32)
+    B, T, R = latent.shape
+    Dr = k_pe.shape[-1]
+    _shape(k_pe, "k_pe", (B, T, Dr))
+    _shape(gain, "gain", (R,))
+    _shape(sin, "sin", cos.shape)
+    if cos.dim() != 2 or cos.shape[1] != Dr // 2:
+        raise ValueError(f"cos should be [table_len, {Dr // 2}], but is {tuple(cos.shape)}")
+    if c_norm is None:
+        c_norm = torch.empty((B, T, R), dtype=torch.float16, device=latent.device)
+    if k_rot is None:
+        k_rot = torch.empty((B, T, Dr), dtype=torch.float16, device=latent.device)
+    _need(c_norm, "c_norm", torch.float16)
+    _need(k_rot, "k_rot", torch.float16)
+    _shape(c_norm, "c_norm", (B, T, R))
+    _shape(k_rot, "k_rot", (B, T, Dr))
+    if pos is not None:
+        _need(pos, "pos", torch.int32)
+        _shape(pos, "pos", (B, T))
+    check("mla_latent_prepare",
+          _lib.load().mla_latent_prepare(_ptr(latent), _ptr(gain), float(eps), _ptr(k_pe), _ptr(cos), _ptr(sin),
+                                         cos.shape[0], _ptr(pos), B, T, R, Dr, pairing_code(pairing), _ptr(c_norm),
+                                         _ptr(k_rot), _stream(latent)))
+    return c_norm, k_rot
 
 
 def _layout_code(v_layout: str) -> int:

@@ -127,6 +127,23 @@ mla_status mla_latent_rmsnorm(const mla_bf16* x, const mla_bf16* w, float eps, u
   return hip_status(mla::launch_rmsnorm(x, w, eps, y, n, R, MLA_DTYPE_FP16, stream));
 }
 
+mla_status mla_latent_prepare(const mla_bf16* latent, const mla_bf16* gain, float eps, const mla_bf16* k_pe,
+                              const float* cos, const float* sin, int32_t table_len, const int32_t* pos, int32_t B,
+                              int32_t T, int32_t R, int32_t Dr, int32_t pairing, uint16_t* c_norm, uint16_t* k_rot,
+                              hipStream_t stream) {
+  if (B < 0 || T < 0 || R < 8 || R > 4096 || (R % 8) || Dr < 2 || Dr > 256 || (Dr & 1)) return MLA_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return MLA_ERR_SHAPE;
+  if (!pairing_ok(pairing)) return MLA_ERR_ROPE_TYPE;
+  if ((int64_t)B * T > ((int64_t)1 << 31) - 1 || (int64_t)B * T * R > kMaxElems) return MLA_ERR_SHAPE;
+  if ((int64_t)B * T == 0) return MLA_OK;
+  if (!latent || !gain || !k_pe || !cos || !sin || !c_norm || !k_rot) return MLA_ERR_NULL;
+  if (table_len < 1 || (!pos && T > table_len)) return MLA_ERR_SHAPE;
+  if (!aligned16(latent) || !aligned16(gain) || !aligned16(c_norm)) return MLA_ERR_SHAPE;
+  clear_stale_error();
+  mla::LatentPrepareArgs a{latent, gain, eps, c_norm, k_pe, cos, sin, table_len, pos, k_rot, B * T, T, R, Dr, pairing};
+  return hip_status(mla::launch_latent_prepare(a, stream));
+}
+
 mla_status mla_rmsnorm(const mla_bf16* x, const mla_bf16* w, float eps, uint16_t* y, int32_t n, int32_t R,
                        int32_t out_dtype, hipStream_t stream) {
   if (!dtype_ok(out_dtype)) return MLA_ERR_UNSUPPORTED;

@@ -27,6 +27,24 @@ hipError_t launch_rope_table(const RopeResolved& r, int n_pos, float* cos_out, f
 hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* w, float eps, uint16_t* y, int n, int R, int out_dtype,
                           hipStream_t stream);
 
+// latent RMSNorm (fp16 out) and the rotation of each token's shared rotary
+// key (fp16 out) in one launch; R a multiple of 8 (<= 4096), rows 16-byte
+// aligned
+struct LatentPrepareArgs {
+  const uint16_t* x;     // [n, R] bf16 latent
+  const uint16_t* w;     // [R] bf16 gain
+  float eps;
+  uint16_t* y;           // [n, R] fp16
+  const uint16_t* k_pe;  // [n, Dr] bf16, n = B*T
+  const float* cos;
+  const float* sin;
+  int table_len;
+  const int32_t* pos;    // [n] or null (= t)
+  uint16_t* k_rot;       // [n, Dr] fp16
+  int n, T, R, Dr, pairing;
+};
+hipError_t launch_latent_prepare(const LatentPrepareArgs& a, hipStream_t stream);
+
 struct ExpandArgs {
   const uint16_t* c;  // [B*T, R] normalised latent, fp16
   const uint16_t* W;  // [N, R], N = H*(Dn+Dv)

@@ -13,17 +13,14 @@
 
 namespace mla {
 
-// Rows whose width R is a multiple of 8 and at most 512*NCH: each lane keeps
-// NCH chunks of 8 elements in registers (chunk c of lane l covers columns
-// 8*(l + 64*c) .. +8).
+// One row whose width R is a multiple of 8 and at most 512*NCH, by one
+// wavefront: each lane keeps NCH chunks of 8 elements in registers (chunk c
+// of lane l covers columns 8*(l + 64*c) .. +8).
 template <int NCH, class OT>
-__global__ void __launch_bounds__(256) rmsnorm_vec_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-                                                          float eps, uint16_t* __restrict__ y, int n, int R) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= n) return;
+__device__ __forceinline__ void rms_row(const uint16_t* __restrict__ xrow, const uint16_t* __restrict__ w, float eps,
+                                        uint16_t* __restrict__ yrow, int R, int lane) {
   const int nch = R >> 3;
-  const u32x4* xr = reinterpret_cast<const u32x4*>(x + (size_t)row * R);
+  const u32x4* xr = reinterpret_cast<const u32x4*>(xrow);
   u32x4 v[NCH];
   float ss = 0.f;
 #pragma unroll
@@ -42,7 +39,7 @@ __global__ void __launch_bounds__(256) rmsnorm_vec_kernel(const uint16_t* __rest
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)R + eps);
   const u32x4* wr = reinterpret_cast<const u32x4*>(w);
-  u32x4* yr = reinterpret_cast<u32x4*>(y + (size_t)row * R);
+  u32x4* yr = reinterpret_cast<u32x4*>(yrow);
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int ch = lane + 64 * c;
@@ -57,6 +54,43 @@ __global__ void __launch_bounds__(256) rmsnorm_vec_kernel(const uint16_t* __rest
       }
       yr[ch] = o;
     }
+  }
+}
+
+template <int NCH, class OT>
+__global__ void __launch_bounds__(256) rmsnorm_vec_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                                                          float eps, uint16_t* __restrict__ y, int n, int R) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  rms_row<NCH, OT>(x + (size_t)row * R, w, eps, y + (size_t)row * R, R, threadIdx.x & 63);
+}
+
+// The latent RMSNorm of a token and the rotation of its shared rotary key in
+// one pass (one wavefront per token): the key of token (b, t) is rotated once
+// at pos[b*T + t] (t when pos is null) and written to k_rot[b, t, :] in fp16,
+// the form the prefill attention reads for every head (Kimi-K2 "Query content
+// heads", section "Join query parts": the rotary key is rotated at its
+// position; GLM-5 "Normalized key-value latent": one rotary key per token,
+// shared by all heads).
+template <int NCH>
+__global__ void __launch_bounds__(256) latent_prepare_kernel(LatentPrepareArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= a.n) return;
+  rms_row<NCH, F16>(a.x + (size_t)row * a.R, a.w, a.eps, a.y + (size_t)row * a.R, a.R, lane);
+  const int half = a.Dr >> 1;
+  int p = a.pos ? a.pos[row] : row % a.T;
+  p = min(max(p, 0), a.table_len - 1);
+  const uint16_t* src = a.k_pe + (size_t)row * a.Dr;
+  uint16_t* dst = a.k_rot + (size_t)row * a.Dr;
+  for (int i = lane; i < half; i += 64) {
+    const int ia = a.pairing ? 2 * i : i;
+    const int ib = a.pairing ? 2 * i + 1 : i + half;
+    const float c = a.cos[(size_t)p * half + i];
+    const float s = a.sin[(size_t)p * half + i];
+    const float xa = bf2f(src[ia]), xb = bf2f(src[ib]);
+    dst[ia] = f2h(xa * c - xb * s);
+    dst[ib] = f2h(xb * c + xa * s);
   }
 }
 
@@ -101,6 +135,17 @@ hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* w, float eps, uint1
     launch_rmsnorm_t<BF16>(x, w, eps, y, n, R, stream);
   else
     launch_rmsnorm_t<F16>(x, w, eps, y, n, R, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_latent_prepare(const LatentPrepareArgs& a, hipStream_t stream) {
+  const dim3 grid((a.n + 3) / 4), block(256);
+  if (a.R <= 512)
+    hipLaunchKernelGGL(latent_prepare_kernel<1>, grid, block, 0, stream, a);
+  else if (a.R <= 1024)
+    hipLaunchKernelGGL(latent_prepare_kernel<2>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(latent_prepare_kernel<8>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

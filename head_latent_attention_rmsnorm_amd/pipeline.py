@@ -1,8 +1,9 @@
 """The whole forward path as a sequence of library calls (no arithmetic here).
 
-prefill_forward: rope table -> latent RMSNorm -> kv_b_proj expansion ->
-causal attention with the rotary step fused in (Kimi-K2 "Query content
-heads", "Join query parts"; equation page "Read the equation").
+prefill_forward: latent RMSNorm with the shared rotary key's rotation ->
+kv_b_proj expansion -> causal attention with the query's rotation fused in
+(Kimi-K2 "Query content heads", "Join query parts"; equation page "Read the
+equation"); the cos/sin table is built once per length (build_table).
 decode_step: latent RMSNorm of the new token -> kv_b_proj expansion appended
 into the expanded cache with its rotated shared key -> split-K decode
 attention (same sections, with the expanded-cache update).
@@ -32,39 +33,43 @@ def build_table(rope: api.RopeParams, n_pos: int, qk_head_dim: int, device="cuda
 
 @dataclass
 class PrefillBuffers:
-    c_norm: torch.Tensor
-    k_nope: torch.Tensor
-    v: torch.Tensor  # V^T [B, H, Dv, round8(T)]
-    out: torch.Tensor
-    workspace: Optional[torch.Tensor] = None
+    c_norm: torch.Tensor  # [B, T, R] fp16
+    k_rot: torch.Tensor   # [B, T, Dr] fp16, the rotated shared rotary key
+    k_nope: torch.Tensor  # [B, H, T, Dn] fp16
+    v: torch.Tensor       # V^T [B, H, Dv, round8(T)] fp16
+    out: torch.Tensor     # [B, H, T, Dv] bf16
 
 
-def alloc_prefill(B, T, H, R, Dn, Dr, Dv, device="cuda", kv_dtype=torch.float16) -> PrefillBuffers:
-    """Intermediate buffers; k_nope and v in `kv_dtype` (fp16 by default: same
-    size and MFMA rate as bf16 on gfx950, three more significant bits). The
-    values are kept transposed (V^T), the layout the attention reads."""
+def alloc_prefill(B, T, H, R, Dn, Dr, Dv, device="cuda") -> PrefillBuffers:
+    """Intermediate buffers; the normalised latent, the rotated key, k_nope and
+    v in fp16 (same size and MFMA rate as bf16 on gfx950, three more
+    significant bits). The values are kept transposed (V^T), the layout the
+    attention reads."""
     return PrefillBuffers(
         c_norm=torch.empty((B, T, R), dtype=torch.float16, device=device),
-        k_nope=torch.empty((B, H, T, Dn), dtype=kv_dtype, device=device),
-        v=torch.empty((B, H, Dv, api.round8(T)), dtype=kv_dtype, device=device),
+        k_rot=torch.empty((B, T, Dr), dtype=torch.float16, device=device),
+        k_nope=torch.empty((B, H, T, Dn), dtype=torch.float16, device=device),
+        v=torch.empty((B, H, Dv, api.round8(T)), dtype=torch.float16, device=device),
         out=torch.empty((B, H, T, Dv), dtype=torch.bfloat16, device=device),
-        workspace=torch.empty((((B * T * Dr * 2) + 255) // 256 * 256,), dtype=torch.uint8, device=device),
     )
 
 
 def prefill_forward(q, latent, k_pe, gain, W, table: RopeTable, Dn: int, Dv: int, pairing="half", eps: float = 1e-6,
-                    bufs: Optional[PrefillBuffers] = None, return_lse: bool = False, kv_dtype=torch.float16):
+                    bufs: Optional[PrefillBuffers] = None, return_lse: bool = False):
     """q [B,H,T,Dn+Dr], latent [B,T,R], k_pe [B,T,Dr], gain [R], W [H*(Dn+Dv),R]
-    (all bf16 on the GPU) -> out [B,H,T,Dv] bf16."""
+    (all bf16 on the GPU) -> out [B,H,T,Dv] bf16. Three launches and the
+    attention: latent RMSNorm with the key rotation, the two expansion
+    launches, then the causal attention over the prepared operands."""
     B, H, T, _ = q.shape
     R = latent.shape[-1]
     Dr = k_pe.shape[-1]
     if bufs is None:
-        bufs = alloc_prefill(B, T, H, R, Dn, Dr, Dv, q.device, kv_dtype)
-    api.mla_latent_rmsnorm(latent, gain, eps, out=bufs.c_norm)
+        bufs = alloc_prefill(B, T, H, R, Dn, Dr, Dv, q.device)
+    api.mla_latent_prepare(latent, gain, eps, k_pe, table.cos, table.sin, pairing, c_norm=bufs.c_norm,
+                           k_rot=bufs.k_rot)
     api.mla_kv_expand(bufs.c_norm, W, H, Dn, Dv, k=bufs.k_nope, v=bufs.v, v_layout="cols")
-    return api.mla_prefill_attention(q, bufs.k_nope, k_pe, bufs.v, table.cos, table.sin, table.scale, pairing,
-                                     return_lse=return_lse, out=bufs.out, workspace=bufs.workspace, v_layout="cols")
+    return api.mla_prefill_attention_cached(q, bufs.k_nope, bufs.k_rot, bufs.v, 0, table.cos, table.sin, table.scale,
+                                            pairing, return_lse=return_lse, out=bufs.out)
 
 
 def decode_step(q, latent, k_pe, gain, W, k_cache, v_cache, seq_len, q_pos, slot: int, table: RopeTable, Dn: int,

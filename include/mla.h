@@ -154,6 +154,28 @@ mla_status mla_softmax_scale(const mla_rope_params* p, int32_t qk_head_dim, doub
 mla_status mla_latent_rmsnorm(const mla_bf16* x, const mla_bf16* w, float eps, uint16_t* y, int32_t n,
                               int32_t R, hipStream_t stream);
 
+/* The latent RMSNorm and the rotation of the shared rotary key in one pass
+ * over the tokens [eq; GLM-kv "Key-value compression"; K2-query "Join query
+ * parts": the rotary key is rotated at its position, once per token, and
+ * shared by all heads]:
+ *   c_norm[b, t, :] = mla_latent_rmsnorm of latent[b, t, :] (fp16 out)
+ *   k_rot[b, t, :]  = rot(k_pe[b, t, :], pos[b, t]) (pos NULL = t), fp16
+ * k_rot is the rotated-key operand of mla_prefill_attention_cached (with
+ * past = 0 and Tcap = T, the whole prefill), so the attention needs no
+ * rotation pass of its own.
+ * Args: latent device bf16 [B, T, R] (R a multiple of 8, 8..4096); gain
+ *   device bf16 [R]; eps >= 0; k_pe device bf16 [B, T, Dr] (Dr even,
+ *   2..256); cos/sin device fp32 [table_len, Dr/2]; pos device int32
+ *   [B, T] or NULL (then table_len >= T); c_norm device fp16 [B, T, R];
+ *   k_rot device fp16 [B, T, Dr]. latent, gain and c_norm 16-byte aligned.
+ *   B*T == 0 is a no-op.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_ROPE_TYPE, MLA_ERR_HIP. */
+mla_status mla_latent_prepare(const mla_bf16* latent, const mla_bf16* gain, float eps,
+                              const mla_bf16* k_pe, const float* cos, const float* sin,
+                              int32_t table_len, const int32_t* pos, int32_t B, int32_t T,
+                              int32_t R, int32_t Dr, int32_t pairing, uint16_t* c_norm,
+                              uint16_t* k_rot, hipStream_t stream);
+
 /* kv_b_proj up-projection and head split [eq; GLM-kv expand_kv]:
  *   kv[b, t, :] = c_norm[b, t, :] . W^T, viewed [H, Dn+Dv]; for each head h
  *   k[b, h, t_off + t, 0:Dn]  = kv[b, t, h*(Dn+Dv) + 0 .. Dn)

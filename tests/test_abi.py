@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared()
-    assert len(names) == 16
+    assert len(names) == 17
     assert sorted(_lib.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -81,6 +81,30 @@ def test_rmsnorm_validation(lib):
     assert lib.mla_latent_rmsnorm(FAKE, FAKE, float("nan"), FAKE, 4, 512, None) == SHAPE
     assert lib.mla_latent_rmsnorm(FAKE, FAKE, 1e-6, FAKE, 0, 512, None) == OK  # empty: no-op
     assert lib.mla_latent_rmsnorm(None, None, 1e-6, None, 0, 512, None) == OK
+
+
+def prepare(lib, **kw):
+    a = dict(latent=FAKE, gain=FAKE, eps=1e-6, k_pe=FAKE, cos=FAKE, sin=FAKE, table_len=8192, pos=None, B=2, T=8192,
+             R=512, Dr=64, pairing=0, c_norm=FAKE, k_rot=FAKE)
+    a.update(kw)
+    return lib.mla_latent_prepare(a["latent"], a["gain"], ctypes.c_float(a["eps"]), a["k_pe"], a["cos"], a["sin"],
+                                  a["table_len"], a["pos"], a["B"], a["T"], a["R"], a["Dr"], a["pairing"],
+                                  a["c_norm"], a["k_rot"], None)
+
+
+def test_latent_prepare_validation(lib):
+    assert prepare(lib, latent=None) == NULL
+    assert prepare(lib, k_rot=None) == NULL
+    assert prepare(lib, cos=None) == NULL
+    assert prepare(lib, R=100) == SHAPE      # not a multiple of 8
+    assert prepare(lib, R=8192) == SHAPE     # wider than 4096
+    assert prepare(lib, Dr=63) == SHAPE
+    assert prepare(lib, eps=-1.0) == SHAPE
+    assert prepare(lib, table_len=100) == SHAPE  # positions 0..T-1 need T table rows
+    assert prepare(lib, pairing=7) == ROPE
+    assert prepare(lib, latent=FAKE + 8) == SHAPE  # 16-byte alignment
+    assert prepare(lib, B=0) == OK
+    assert prepare(lib, T=0, latent=None) == OK
 
 
 def expand(lib, **kw):

@@ -79,6 +79,39 @@ def test_rmsnorm(n, R):
     assert np.all(d <= np.abs(ref) * (2.0 ** -11 + R * u + 8 * u) + 2.0 ** -25), (d / np.abs(ref)).max()
 
 
+@pytest.mark.parametrize("pairing", ["half", "interleaved"])
+def test_latent_prepare(pairing):
+    """The fused pass: the latent RMSNorm (as mla_latent_rmsnorm, bit for
+    bit) and each token's rotary key rotated at its position, within one
+    fp16 rounding of the fp64 rotation of the fp32 table entries."""
+    B, T, R, Dr = 3, 301, 512, 64
+    say(f"[latent prepare] B={B} T={T} {pairing}")
+    g = torch.Generator().manual_seed(91)
+    x = (torch.randn(B, T, R, generator=g) * 3).to(torch.bfloat16)
+    w = (1 + 0.3 * torch.randn(R, generator=g)).to(torch.bfloat16)
+    kpe = torch.randn(B, T, Dr, generator=g).to(torch.bfloat16)
+    spec = workloads.YARN_KIMI
+    tab = pipeline.build_table(api.params_from(spec, Dr), T, 192)
+    c, kr = api.mla_latent_prepare(x.cuda(), w.cuda(), 1e-6, kpe.cuda(), tab.cos, tab.sin, pairing)
+    torch.cuda.synchronize()
+    assert torch.equal(c, api.mla_latent_rmsnorm(x.cuda(), w.cuda(), 1e-6))
+    cos, sin = f64(tab.cos.cpu()), f64(tab.sin.cpu())
+    ref = O.rotate(f64(kpe), cos[None], sin[None], pairing)
+    # fp32 products and sum of bf16 inputs and fp32 table entries (a few u),
+    # then one fp16 rounding (2^-11 relative, 2^-25 absolute below 2^-14)
+    bound = np.abs(ref) * 2.0 ** -11 + 4 * 2.0 ** -24 * (np.abs(f64(kpe)) * 2).sum(-1, keepdims=True) + 2.0 ** -25
+    assert np.all(np.abs(f64(kr.cpu()) - ref) <= bound)
+    # explicit positions (offset 40): the rotation follows them
+    pos = (torch.arange(T, dtype=torch.int32)[None, :] + 40 * torch.arange(B, dtype=torch.int32)[:, None])
+    tab2 = pipeline.build_table(api.params_from(spec, Dr), T + 80, 192)
+    _, kr2 = api.mla_latent_prepare(x.cuda(), w.cuda(), 1e-6, kpe.cuda(), tab2.cos, tab2.sin, pairing,
+                                    pos=pos.cuda())
+    torch.cuda.synchronize()
+    cos2, sin2 = f64(tab2.cos.cpu())[pos.numpy()], f64(tab2.sin.cpu())[pos.numpy()]
+    ref2 = O.rotate(f64(kpe), cos2, sin2, pairing)
+    assert np.all(np.abs(f64(kr2.cpu()) - ref2) <= np.abs(ref2) * 2.0 ** -11 + 1e-5)
+
+
 # --------------------------------------------------------------------- kv_b_proj
 
 EXPAND_SHAPES = [
