@@ -24,6 +24,22 @@
  *               cache keeps the normalised latent and the rotated rotary
  *               key per token and re-expands them on every call.
  *
+ * Interface notes (the shapes and scale rules are the pages'; these are the
+ * choices made around them, each stated again at its call):
+ *   - intermediates in fp16, not the model dtype: the normalised latent
+ *     (mla_latent_rmsnorm, mla_latent_prepare), the expanded keys and values
+ *     and the attention operands, for three more significant bits at the same
+ *     size and MFMA rate (bf16 keys/values remain selectable where the
+ *     result stays within bounds: expansion and decode caches);
+ *   - values may be handed over transposed (V^T, MLA_V_COLS), the layout the
+ *     P.V product reads; the pages' row layout is accepted and transposed;
+ *   - every call that reads the cos/sin table takes its length (table_len),
+ *     so that device-side positions can be clamped into it;
+ *   - calls that need scratch memory take a caller workspace (query its size
+ *     with workspace == NULL), except mla_decode_attention_noalloc;
+ *   - mla_rope_table_build returns the softmax-scale multiplier in double,
+ *     as the host computes it.
+ *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE memory owned by the caller; the library
  *     never allocates, frees or retains them and keeps no global state.
@@ -80,8 +96,12 @@ typedef enum { MLA_PAIR_HALF = 0, MLA_PAIR_INTERLEAVED = 1 } mla_rope_pairing;
  * of the attention MFMA operands. The pages keep them in the model dtype
  * (bf16). FP16 has the same size and MFMA rate on gfx950 and three more
  * significant bits, which keeps the whole path inside its error budget; it
- * requires |values| < 65504 (larger ones overflow to inf). Queries, rotary
- * keys and outputs stay bf16 at the boundary in both modes. */
+ * requires |values| < 65504: a larger key or value becomes inf in the fp16
+ * expansion, and the attention outputs that touch it (and the other rows of
+ * its 64-key tile, through the zero weight of a masked key times inf) come
+ * out inf or NaN, never finite and wrong. The same bound holds for the
+ * normalised latent (fp16) and for the query times scale * log2(e).
+ * Queries, rotary keys and outputs stay bf16 at the boundary. */
 typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP16 = 1 } mla_dtype;
 
 /* Layout of the expanded values. ROWS: [B, H, T, Dv], the layout the pages

@@ -449,6 +449,38 @@ def test_prefill_rejects_bf16_intermediates():
     assert torch.all(out == 7.0)
 
 
+def test_prefill_fp16_range():
+    """fp16 intermediates hold |x| < 65504. kv_b_proj weights scaled so that
+    keys and values reach about 2^16 overflow to inf in the fp16 expansion,
+    and the attention then gives non-finite outputs, never finite wrong ones
+    (the documented outcome). At 2^10 (keys and values near 1e3, 20 times
+    below the limit) everything stays finite and matches the oracle in
+    relative terms."""
+    w = workloads.custom(name="k2-range", B=1, T=200, H=2, R=512, Dn=128, Dr=64, Dv=128, seed=45,
+                         rope=workloads.YARN_KIMI)
+    inp = workloads.make_inputs(w)
+    for mul, finite in ((2.0 ** 16, False), (2.0 ** 10, True)):
+        sub = dict(inp)
+        sub["W"] = (inp["W"].float() * mul).to(torch.bfloat16)
+        g = to_gpu(sub)
+        tab = table(w)
+        c = api.mla_latent_rmsnorm(g["latent"], g["gain"], w.eps)
+        kn, vt = api.mla_kv_expand(c, g["W"], w.H, w.Dn, w.Dv, v_layout="cols")
+        out = api.mla_prefill_attention(g["q"], kn, g["k_pe"], vt, tab.cos, tab.sin, tab.scale, w.pairing,
+                                        v_layout="cols")
+        torch.cuda.synchronize()
+        say(f"[prefill fp16 range] W x {mul:g}: {int(torch.isinf(kn).sum())} inf keys, "
+            f"{int(torch.isfinite(out).sum())} finite outputs of {out.numel()}")
+        if finite:
+            assert torch.isfinite(kn).all() and torch.isfinite(vt).all() and torch.isfinite(out).all()
+            ref = O.prefill(w, sub)
+            _, rl = errors(f64(out.cpu()), ref)
+            assert rl <= REL_L2, rl
+        else:
+            assert torch.isinf(kn).any() and torch.isinf(vt).any()
+            assert not torch.isfinite(out).any()
+
+
 def test_prefill_empty_is_noop():
     w = workloads.custom(B=1, T=0, H=2, R=512, Dn=128, Dr=64, Dv=128)
     q = torch.empty((1, 2, 0, 192), dtype=torch.bfloat16, device="cuda")
