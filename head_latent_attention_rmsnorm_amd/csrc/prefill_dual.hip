@@ -25,10 +25,18 @@
 //    0-31, 12 for keys 32-63, 8 of P V for keys 0-31, 8 for keys 32-63. The
 //    read of step i + PF is issued in step i, so each fragment has PF steps
 //    (2*PF MFMAs) to arrive. The softmax of keys 0-31 (exp2, conversion,
-//    row sums) is cut into pieces issued between the score MFMAs of keys
+//    row sums) runs one score at a time between the score MFMAs of keys
 //    32-63, and the softmax of keys 32-63 between the P V MFMAs of keys 0-31:
-//    a wave's VALU work runs while its own MFMAs execute. Scheduling fences
-//    between steps keep that order.
+//    a wave's VALU work runs while its own MFMAs execute;
+//  - a wave that issues an MFMA while its previous one still occupies the
+//    unit stalls until it leaves, so a step's VALU work is split over the
+//    gaps after each of its two MFMAs, and no gap gets more than the 32
+//    cycles an MFMA takes where that can be helped: one score per half-step,
+//    the score accumulators copied out to vector registers 8 at a time over
+//    four half-steps (one 16-register copy at the first use would idle the
+//    MFMA pipe for ~100 cycles), each P packed where it is computed rather
+//    than after the rare-path branch. Scheduling fences around every MFMA
+//    keep that order.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -194,67 +202,93 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
     for (int i = 0; i < LPW; ++i) lds_load16(rs[i], &smem[buf][(wave + NW * i) * 64], voff[i] + key0 * vstep[i]);
   };
 
+  // rotary positions of the lane's two query rows (looked up first: with
+  // positions given, the wait for them then covers nothing else)
+  int prow[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int tq = qlo + 32 * r + l32;
+    prow[r] = a.pos ? a.pos[(size_t)b * T + (tq < T ? tq : 0)] : past + tq;
+    prow[r] = min(max(prow[r], 0), a.table_len - 1);
+  }
+
   // the first tile's loads go out before the query's, so that both
   // latencies overlap
   issue(0, 0);
 
   // ---- prologue: rotated (and in fp16 mode pre-scaled) query fragments of
-  // both blocks
+  // both blocks. Every load goes out before any arithmetic: the query chunks
+  // of both blocks, then the cos / sin of the lane's rotary pairs, so the
+  // whole prologue waits for one memory round trip. Rotary chunk cc (16
+  // dims, dims 8g..8g+7 in this lane) pairs dims within the chunk
+  // (interleaved: 4 pairs) or with chunk cc +- RC/2 (half: 8 pairs, the
+  // partner dims in the same lane); either way a lane touches DR/4 pairs,
+  // DR/16 runs of four.
+  constexpr int RC = DR / 16;
+  static_assert(DN % 16 == 0 && DR % 32 == 0, "rotary chunks of 16 dims, two halves");
   u32x4 qf[2][QC];
+  f32x4 cw[2][RC], sw[2][RC];
+  const int pairing = a.pairing;
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int tq = qlo + 32 * r + l32;
-    const bool valid = tq < T;
-    int p = a.pos ? a.pos[(size_t)b * T + (valid ? tq : 0)] : past + tq;
-    p = min(max(p, 0), a.table_len - 1);
-    const uint16_t* qrow = qg + (size_t)(valid ? tq : 0) * DQK;
-    const float* crow = a.cos + (size_t)p * (DR / 2);
-    const float* srow = a.sin + (size_t)p * (DR / 2);
+    const int trow = tq < T ? tq : 0;
+    const int p = prow[r];
+    const uint16_t* qrow = qg + (size_t)trow * DQK;
+#pragma unroll
+    for (int c = 0; c < QC; ++c) qf[r][c] = *reinterpret_cast<const u32x4*>(qrow + 16 * c + 8 * g);
+#pragma unroll
+    for (int k = 0; k < RC; ++k) {
+      // first pair of run k: half pairing, chunks k/2 and k/2 + RC/2, its
+      // (k&1)-th four pairs; interleaved, chunk k
+      const int pi = pairing ? 8 * k + 4 * g : 16 * (k >> 1) + 8 * g + 4 * (k & 1);
+      cw[r][k] = *reinterpret_cast<const f32x4*>(a.cos + (size_t)p * (DR / 2) + pi);
+      sw[r][k] = *reinterpret_cast<const f32x4*>(a.sin + (size_t)p * (DR / 2) + pi);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (qlo + 32 * r + l32 >= T) {
+#pragma unroll
+      for (int c = 0; c < QC; ++c) qf[r][c] = u32x4{0u, 0u, 0u, 0u};
+    }
+    auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
+    auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
+    u32x4 rot[RC];
+    if (!pairing) {
+#pragma unroll
+      for (int cc = 0; cc < RC; ++cc) {
+        const bool first = cc < RC / 2;
+        const u32x4 x = qf[r][DN / 16 + cc], y = qf[r][DN / 16 + (first ? cc + RC / 2 : cc - RC / 2)];
+        const int k0 = 2 * (cc % (RC / 2));
+        const float sgn = first ? -1.0f : 1.0f;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const f32x4 cs = cw[r][k0 + e2 / 2], sn = sw[r][k0 + e2 / 2];
+          const int i0 = 2 * (e2 % 2);
+          rot[cc][e2] = ET::pack2((lo(x[e2]) * cs[i0] + sgn * (lo(y[e2]) * sn[i0])) * qmul,
+                                  (hi(x[e2]) * cs[i0 + 1] + sgn * (hi(y[e2]) * sn[i0 + 1])) * qmul);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < RC; ++cc) {
+        const u32x4 x = qf[r][DN / 16 + cc];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float cs = cw[r][cc][e2], sn = sw[r][cc][e2];
+          rot[cc][e2] = ET::pack2((lo(x[e2]) * cs - hi(x[e2]) * sn) * qmul, (hi(x[e2]) * cs + lo(x[e2]) * sn) * qmul);
+        }
+      }
+    }
 #pragma unroll
     for (int c = 0; c < QC; ++c) {
-      const int d0 = 16 * c + 8 * g;
-      u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + d0);
-      if (!valid) raw = u32x4{0u, 0u, 0u, 0u};
-      if (d0 >= DN) {
-        // rotary part: each 8-element chunk uses 8 consecutive pairs (half
-        // pairing: the partner is the same chunk of the other half) or 4
-        // (interleaved: the partner is the other half of each word)
-        const int re0 = d0 - DN;
-        u32x4 outv;
-        if (!a.pairing) {
-          const bool first = re0 < DR / 2;
-          const int pi0 = first ? re0 : re0 - DR / 2;
-          u32x4 partner = *reinterpret_cast<const u32x4*>(qrow + DN + (first ? re0 + DR / 2 : re0 - DR / 2));
-          if (!valid) partner = u32x4{0u, 0u, 0u, 0u};
-          const f32x4 c0 = *reinterpret_cast<const f32x4*>(crow + pi0);
-          const f32x4 c1 = *reinterpret_cast<const f32x4*>(crow + pi0 + 4);
-          const f32x4 s0 = *reinterpret_cast<const f32x4*>(srow + pi0);
-          const f32x4 s1 = *reinterpret_cast<const f32x4*>(srow + pi0 + 4);
-          const float sgn = first ? -1.0f : 1.0f;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const float cs0 = e2 < 2 ? c0[2 * e2] : c1[2 * e2 - 4], cs1 = e2 < 2 ? c0[2 * e2 + 1] : c1[2 * e2 - 3];
-            const float sn0 = e2 < 2 ? s0[2 * e2] : s1[2 * e2 - 4], sn1 = e2 < 2 ? s0[2 * e2 + 1] : s1[2 * e2 - 3];
-            const float x0 = __uint_as_float(raw[e2] << 16), x1 = __uint_as_float(raw[e2] & 0xffff0000u);
-            const float p0 = __uint_as_float(partner[e2] << 16), p1 = __uint_as_float(partner[e2] & 0xffff0000u);
-            outv[e2] = ET::pack2((x0 * cs0 + sgn * (p0 * sn0)) * qmul, (x1 * cs1 + sgn * (p1 * sn1)) * qmul);
-          }
-        } else {
-          const f32x4 cs = *reinterpret_cast<const f32x4*>(crow + (re0 >> 1));
-          const f32x4 sn = *reinterpret_cast<const f32x4*>(srow + (re0 >> 1));
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const float x0 = __uint_as_float(raw[e2] << 16), x1 = __uint_as_float(raw[e2] & 0xffff0000u);
-            outv[e2] = ET::pack2((x0 * cs[e2] - x1 * sn[e2]) * qmul, (x1 * cs[e2] + x0 * sn[e2]) * qmul);
-          }
-        }
-        raw = outv;
+      if (c >= DN / 16) {
+        qf[r][c] = rot[c - DN / 16];
       } else if (FOLD || ET::code != BF16::code) {
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2)
-          raw[e2] = ET::pack2(__uint_as_float(raw[e2] << 16) * qmul, __uint_as_float(raw[e2] & 0xffff0000u) * qmul);
+        for (int e2 = 0; e2 < 4; ++e2) qf[r][c][e2] = ET::pack2(lo(qf[r][c][e2]) * qmul, hi(qf[r][c][e2]) * qmul);
       }
-      qf[r][c] = raw;
     }
   }
 
@@ -305,84 +339,96 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
     return *reinterpret_cast<const u32x4*>(sb + (KBLK + d * 4 + (st / SWV) * SWV) * 1024 + rdv[st % SWV]);
   };
   // the two MFMAs of a key step (both blocks) and of a value step
-  auto s_mfma = [&](int j, int c, u32x4 f) __attribute__((always_inline)) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      if (c == 0) {
-        if (FOLD) {
-          sacc[j][r] = ET::mma(f, qf[r][0], negm[r]);
-        } else {
-          f32x16 z;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) z[e] = 0.f;
-          sacc[j][r] = ET::mma(f, qf[r][0], z);
-        }
+  // the MFMA of block r of a key step and of a value step
+  auto s_mfma = [&](int j, int c, int r, u32x4 f) __attribute__((always_inline)) {
+    if (c == 0) {
+      if (FOLD) {
+        sacc[j][r] = ET::mma(f, qf[r][0], negm[r]);
       } else {
-        sacc[j][r] = ET::mma(f, qf[r][c], sacc[j][r]);
+        f32x16 z;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) z[e] = 0.f;
+        sacc[j][r] = ET::mma(f, qf[r][0], z);
       }
+    } else {
+      sacc[j][r] = ET::mma(f, qf[r][c], sacc[j][r]);
     }
   };
-  auto pv_mfma = [&](int j, int d, int s, u32x4 f) __attribute__((always_inline)) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      oacc[r][d] = ET::mma(f, pf[j][r][s], oacc[r][d]);
-      in_agpr(oacc[r][d]);
-    }
+  auto pv_mfma = [&](int j, int d, int s, int r, u32x4 f) __attribute__((always_inline)) {
+    oacc[r][d] = ET::mma(f, pf[j][r][s], oacc[r][d]);
+    in_agpr(oacc[r][d]);
   };
 
-  // softmax piece u (0..15) of sub-tile j: block u / 8, scores 2(u%8) and
-  // 2(u%8)+1. prep scales (bf16 mode) and masks (diagonal tiles) them in
-  // place, expo turns them into P (16-bit, packed as the B operand of P V)
-  // and adds them to the lane's sum
-  auto prep = [&](int j, int u, int key0, bool diag) __attribute__((always_inline)) {
-    const int r = u / 8, e = u % 8;
-    float s0 = sacc[j][r][2 * e], s1 = sacc[j][r][2 * e + 1];
-    if (!FOLD) {
-      s0 = fmaf(s0, sl2, -m_ref[r]);
-      s1 = fmaf(s1, sl2, -m_ref[r]);
-    }
-    if (diag) {
-      const int kb = key0 + 32 * j + 16 * (e >> 2) + 8 * g + 2 * (e & 3);
-      const int qpos = past + qlo + 32 * r + l32;
-      if (kb > qpos) s0 = -INFINITY;
-      if (kb + 1 > qpos) s1 = -INFINITY;
-    }
-    sacc[j][r][2 * e] = s0;
-    sacc[j][r][2 * e + 1] = s1;
-  };
-  auto expo = [&](int j, int u) __attribute__((always_inline)) {
-    const int r = u / 8, e = u % 8;
-    const float p0 = __builtin_amdgcn_exp2f(sacc[j][r][2 * e]), p1 = __builtin_amdgcn_exp2f(sacc[j][r][2 * e + 1]);
-    pf[j][r][e >> 2][e & 3] = ET::pack2(p0, p1);
-    // row sums in fp32 adds (a packed dot product would not overlap the MFMAs)
-    ts[j][r] = (e == 0) ? p0 + p1 : ts[j][r] + p0 + p1;
-  };
-  // pieces [u0, u1) of sub-tile j
-  auto pieces = [&](int j, int u0, int u1, int key0, bool diag) __attribute__((always_inline)) {
+  // Softmax of sub-tile j, one score at a time. Once a block's score chain
+  // is complete its 16 accumulators are copied to vector registers in two
+  // halves of 8, in successive half-steps (copy_half; one copy of all 16 at
+  // the first use would stall the MFMA pipe), and the softmax reads the
+  // copies: score v (0..31) is element v % 16 of block v / 16. Each score is
+  // scaled (bf16 mode), masked (diagonal tiles) and turned into P; the odd
+  // score of a pair packs both (16-bit, the B operand of P V), pinned where
+  // it is computed. The lane's row sum takes every P in fp32 adds (a packed
+  // dot product would not overlap the MFMAs).
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  f32x8 sv[2][2][2];  // score copies [sub-tile][block][half]
+  float pev[2];       // P of the even score of the pair in progress [sub-tile]
+  auto copy_half = [&](int j, int r, int hh) __attribute__((always_inline)) {
+    in_agpr(sacc[j][r]);  // holds the reads at this point
+    f32x8 t;
 #pragma unroll
-    for (int u = u0; u < u1; ++u) {
-      prep(j, u, key0, diag);
-      expo(j, u);
+    for (int i = 0; i < 8; ++i) t[i] = sacc[j][r][8 * hh + i];
+    in_vgpr(t);
+    sv[j][r][hh] = t;
+  };
+  // score i of block r of sub-tile j as an exp2 argument: scaled (bf16
+  // mode) and masked (diagonal tiles)
+  auto prepped = [&](int j, int r, int i, int key0, bool diag) __attribute__((always_inline)) -> float {
+    float x = sv[j][r][i / 8][i % 8];
+    if (!FOLD) x = fmaf(x, sl2, -m_ref[r]);
+    if (diag) {
+      const int e = i / 2;
+      const int kb = key0 + 32 * j + 16 * (e >> 2) + 8 * g + 2 * (e & 3) + (i & 1);
+      if (kb > past + qlo + 32 * r + l32) x = -INFINITY;
     }
+    return x;
+  };
+  auto put_p = [&](int j, int r, int e, float p0, float p1) __attribute__((always_inline)) {
+    const uint32_t w = ET::pack2(p0, p1);
+    asm volatile("" ::"v"(w));  // packed here, not sunk past the rare-path branch
+    pf[j][r][e >> 2][e & 3] = w;
+  };
+  auto score = [&](int j, int v, int key0, bool diag) __attribute__((always_inline)) {
+    const int r = v / 16, i = v % 16;
+    const float pv = __builtin_amdgcn_exp2f(prepped(j, r, i, key0, diag));
+    ts[j][r] = i == 0 ? pv : ts[j][r] + pv;
+    if (i % 2 == 0) pev[j] = pv;
+    else put_p(j, r, i / 2, pev[j], pv);
+  };
+  // scores [v0, v1) of sub-tile j
+  auto scores = [&](int j, int v0, int v1, int key0, bool diag) __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = v0; v < v1; ++v) score(j, v, key0, diag);
   };
 
   // The rare path after the softmax of sub-tile j: the exact maximum of its
   // scores, and the reference moved to it on the first sub-tile or wherever
   // a score exceeds it by more than the slack (exact: O and the row sum share
-  // the reference). `pend`: the other sub-tile's scores were already
-  // accumulated onto the old -m_ref (fp16 mode) and move with it.
-  auto check = [&](int j, bool pend) __attribute__((always_inline)) {
+  // the reference); P and the row sums of sub-tile j are then recomputed
+  // from its copies. `pend`: the other sub-tile's scores were already
+  // accumulated onto the old -m_ref (fp16 mode, not yet copied) and move
+  // with it.
+  auto check = [&](int j, bool pend, int key0, bool diag) __attribute__((always_inline)) {
     if (__any(!ref_set || ts[j][0] > kSumLimD || ts[j][1] > kSumLimD)) {
+      float shift[2];
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[j][r][i]);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, prepped(j, r, i, key0, diag));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const bool raise = !ref_set || mx > kSlackD;
-        const float shift = raise ? mx : 0.f;
+        shift[r] = raise ? mx : 0.f;
         const float alpha = (raise && ref_set) ? __builtin_amdgcn_exp2f(-mx) : 1.f;
-        m_ref[r] += shift;
+        m_ref[r] += shift[r];
         lsum[r] *= alpha;
 #pragma unroll
         for (int d = 0; d < NO; ++d) {
@@ -393,12 +439,13 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
           for (int i = 0; i < 16; ++i) oacc[r][d][i] *= alpha;
           in_agpr(oacc[r][d]);
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[j][r][i] -= shift;
         if (FOLD) {
           if (pend) {
+            // kept in the accumulation registers, as the common path holds it
+            in_agpr(sacc[1 - j][r]);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[1 - j][r][i] -= shift;
+            for (int i = 0; i < 16; ++i) sacc[1 - j][r][i] -= shift[r];
+            in_agpr(sacc[1 - j][r]);
           }
 #pragma unroll
           for (int i = 0; i < 16; ++i) negm[r][i] = -m_ref[r];
@@ -406,8 +453,20 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
         }
       }
       ref_set = true;
+      // bf16 mode: prepped() now subtracts the moved reference itself
 #pragma unroll
-      for (int u = 0; u < 16; ++u) expo(j, u);
+      for (int r = 0; r < 2; ++r) {
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float c = FOLD ? shift[r] : 0.f;
+          const float p0 = __builtin_amdgcn_exp2f(prepped(j, r, 2 * e, key0, diag) - c);
+          const float p1 = __builtin_amdgcn_exp2f(prepped(j, r, 2 * e + 1, key0, diag) - c);
+          pf[j][r][e >> 2][e & 3] = ET::pack2(p0, p1);
+          t += p0 + p1;
+        }
+        ts[j][r] = t;
+      }
     }
     lsum[0] += ts[j][0];
     lsum[1] += ts[j][1];
@@ -425,17 +484,20 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
     if (id < 32) return kfrag(cur, 1, id - 20);
     return vfrag(cur, 0, (id - 32) / 2, (id - 32) % 2);
   };
-  auto mfma_of = [&](int id, u32x4 f) __attribute__((always_inline)) {
-    if (id < 12) s_mfma(0, id, f);
-    else if (id < 20) pv_mfma(1, (id - 12) / 2, (id - 12) % 2, f);
-    else if (id < 32) s_mfma(1, id - 20, f);
-    else pv_mfma(0, (id - 32) / 2, (id - 32) % 2, f);
+  auto mfma_of = [&](int id, int r, u32x4 f) __attribute__((always_inline)) {
+    if (id < 12) s_mfma(0, id, r, f);
+    else if (id < 20) pv_mfma(1, (id - 12) / 2, (id - 12) % 2, r, f);
+    else if (id < 32) s_mfma(1, id - 20, r, f);
+    else pv_mfma(0, (id - 32) / 2, (id - 32) % 2, r, f);
   };
-  constexpr int PA = 6;  // softmax pieces of a sub-tile issued under its own tile's value steps
-  // n steps; step k is step idat(k) of the numbering above. Each step reads
-  // ahead the fragment of step k + PF, issues its two MFMAs, then `between(k)`
-  // (softmax pieces, tile loads, the rare-path checks). The read-ahead runs
-  // across the checks, so no step waits for a fresh LDS read.
+  constexpr int SA = 12;  // scores of a sub-tile whose softmax runs under its own tile's value steps
+  // n steps; step k is step order_id(k) of the numbering above. Each step
+  // reads ahead the fragment of step k + PF, then issues its two MFMAs (block
+  // 0, block 1), each followed by `between(k, h)` for half h: softmax
+  // scores, tile loads, the rare-path checks, closed by a scheduling fence.
+  // A wave's second MFMA stalls its issue until the first leaves the unit,
+  // so VALU work placed after each of the two keeps both gaps busy. The
+  // read-ahead runs across the checks, so no step waits for a fresh LDS read.
   auto run = [&](const char* cur, const char* prev, auto order_c, auto&& between) __attribute__((always_inline)) {
     constexpr int M = decltype(order_c)::value;
     constexpr int N = order_len(M);
@@ -444,12 +506,34 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
       constexpr int k = decltype(kc)::value;
       fr[k] = fetch(cur, prev, order_id(M, k));
     });
+    // the copies of a finished score chain (last key step: id 11 or 31 at
+    // position kl): block 0 low half after kl's second MFMA, block 0 high
+    // half and block 1 low half in the next step, block 1 high half in the
+    // one after; each after that half-step's own work
+    auto chain_end = [](int kk) { return kk >= 0 && kk < N && (order_id(M, kk) == 11 || order_id(M, kk) == 31); };
+    auto chain_of = [](int kk) { return order_id(M, kk) == 11 ? 0 : 1; };
     static_for<0, N>([&](auto kc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value;
+      constexpr int id = order_id(M, k);
       if constexpr (k + PF < N) fr[(k + PF) % (PF + 1)] = fetch(cur, prev, order_id(M, k + PF));
-      mfma_of(order_id(M, k), fr[k % (PF + 1)]);
-      between(kc);
+      mfma_of(id, 0, fr[k % (PF + 1)]);
+      fence();
+      between(kc, IntC<0>{});
+      if constexpr (chain_end(k - 1)) copy_half(chain_of(k - 1), 0, 1);
+      if constexpr (chain_end(k - 2)) copy_half(chain_of(k - 2), 1, 1);
+      fence();
+      mfma_of(id, 1, fr[k % (PF + 1)]);
+      fence();
+      between(kc, IntC<1>{});
+      if constexpr (chain_end(k)) copy_half(chain_of(k), 0, 0);
+      if constexpr (chain_end(k - 1)) copy_half(chain_of(k - 1), 1, 0);
+      fence();
     });
+  };
+  // scores [v0 + n q / m, v0 + n (q+1) / m) of sub-tile j: the q-th of m
+  // equal shares of n scores starting at v0
+  auto share = [&](int j, int v0, int n, int m, int q, int key0, bool diag) __attribute__((always_inline)) {
+    scores(j, v0 + n * q / m, v0 + n * (q + 1) / m, key0, diag);
   };
   // one of this wave's LDS-direct loads of tile kt into buffer bf
   auto issue_one = [&](int i, int kt, int bf) __attribute__((always_inline)) {
@@ -459,48 +543,55 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
   // One tile in the software pipeline: while the scores of its first 32 keys
   // are multiplied, the softmax of the previous tile's last 32 keys runs on
   // the VALU; then that sub-tile's P V (its values still in the previous
-  // buffer) under the first pieces of this tile's softmax of keys 0-31; then
+  // buffer) under the first scores of this tile's softmax of keys 0-31; then
   // the scores of keys 32-63 under the rest of it; then the P V of keys 0-31
-  // under the first pieces of the softmax of keys 32-63, whose remainder and
+  // under the first scores of the softmax of keys 32-63, whose remainder and
   // P V are left to the next tile. FIRST: no previous tile. The loads of the
   // next tile (nxt >= 0: its index, into buffer nbf) are spread over the
   // first steps, one per two steps.
   auto body = [&](const char* cur, const char* prev, int key0, int nxt, int nbf, auto first_c)
                   __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_c)::value;
-    auto loads = [&](int k) __attribute__((always_inline)) {
-      if (k % 2 == 0 && k / 2 < LPW && nxt >= 0) issue_one(k / 2, nxt, nbf);
+    auto loads = [&](int k, int h) __attribute__((always_inline)) {
+      if (h == 1 && k % 2 == 0 && k / 2 < LPW && nxt >= 0) issue_one(k / 2, nxt, nbf);
     };
     if (!FIRST) {
-      run(cur, prev, IntC<kPipe>{}, [&](auto kc) __attribute__((always_inline)) {
-        constexpr int k = decltype(kc)::value;
-        if (k < 12) pieces(1, PA + (16 - PA) * k / 12, PA + (16 - PA) * (k + 1) / 12, 0, false);
-        else if (k < 20) pieces(0, PA * (k - 12) / 8, PA * (k - 11) / 8, key0, false);
-        else if (k < 32) pieces(0, PA + (16 - PA) * (k - 20) / 12, PA + (16 - PA) * (k - 19) / 12, key0, false);
-        else pieces(1, PA * (k - 32) / 8, PA * (k - 31) / 8, key0, false);
-        loads(k);
-        fence();
-        if (k == 11) check(1, true);
-        if (k == 31) check(0, true);
+      run(cur, prev, IntC<kPipe>{}, [&](auto kc, auto hc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value, h = decltype(hc)::value;
+        if (k < 12) share(1, SA, 32 - SA, 24, 2 * k + h, 0, false);
+        else if (k < 20) share(0, 0, SA, 16, 2 * (k - 12) + h, key0, false);
+        else if (k < 32) share(0, SA, 32 - SA, 24, 2 * (k - 20) + h, key0, false);
+        else share(1, 0, SA, 16, 2 * (k - 32) + h, key0, false);
+        loads(k, h);
+        if (h == 1 && k == 11) {
+          fence();
+          check(1, true, 0, false);
+        }
+        if (h == 1 && k == 31) {
+          fence();
+          check(0, true, key0, false);
+        }
       });
     } else {
-      run(cur, prev, IntC<kFirst>{}, [&](auto kc) __attribute__((always_inline)) {
-        constexpr int k = decltype(kc)::value;
+      run(cur, prev, IntC<kFirst>{}, [&](auto kc, auto hc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value, h = decltype(hc)::value;
         constexpr int id = order_id(kFirst, k);
-        if (id >= 20 && id < 32) pieces(0, 16 * (id - 20) / 12, 16 * (id - 19) / 12, key0, false);
-        if (id >= 32) pieces(1, PA * (id - 32) / 8, PA * (id - 31) / 8, key0, false);
-        loads(k);
-        fence();
-        if (id == 31) check(0, true);
+        if (id >= 20 && id < 32) share(0, 0, 32, 24, 2 * (id - 20) + h, key0, false);
+        if (id >= 32) share(1, 0, SA, 16, 2 * (id - 32) + h, key0, false);
+        loads(k, h);
+        if (h == 1 && id == 31) {
+          fence();
+          check(0, true, key0, false);
+        }
       });
     }
   };
   // the pipeline's tail: the rest of the softmax of the last tile's keys
   // 32-63 and their P V (values in buffer prev)
   auto drain = [&](const char* prev) __attribute__((always_inline)) {
-    pieces(1, PA, 16, 0, false);
-    check(1, false);
-    run(prev, prev, IntC<kDrain>{}, [](auto) { fence(); });
+    scores(1, SA, 32, 0, false);
+    check(1, false, 0, false);
+    run(prev, prev, IntC<kDrain>{}, [](auto, auto) {});
   };
   // A whole tile outside the pipeline, for tiles that cross the wave's
   // diagonal: scores of keys 0-31; scores of keys 32-63 under the masked
@@ -508,13 +599,18 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
   // P V of keys 32-63 (same step numbering, this tile's buffer as the
   // "previous" one).
   auto tile_diag = [&](const char* cur, int key0) __attribute__((always_inline)) {
-    run(cur, cur, IntC<kDiag>{}, [&](auto kc) __attribute__((always_inline)) {
-      constexpr int id = order_id(kDiag, decltype(kc)::value);
-      if (id >= 20 && id < 32) pieces(0, 16 * (id - 20) / 12, 16 * (id - 19) / 12, key0, true);
-      if (id >= 32) pieces(1, 16 * (id - 32) / 8, 16 * (id - 31) / 8, key0, true);
-      fence();
-      if (id == 31) check(0, true);
-      if (id == 39) check(1, false);
+    run(cur, cur, IntC<kDiag>{}, [&](auto kc, auto hc) __attribute__((always_inline)) {
+      constexpr int id = order_id(kDiag, decltype(kc)::value), h = decltype(hc)::value;
+      if (id >= 20 && id < 32) share(0, 0, 32, 24, 2 * (id - 20) + h, key0, true);
+      if (id >= 32) share(1, 0, 32, 16, 2 * (id - 32) + h, key0, true);
+      if (h == 1 && id == 31) {
+        fence();
+        check(0, true, key0, true);
+      }
+      if (h == 1 && id == 39) {
+        fence();
+        check(1, false, key0, true);
+      }
     });
   };
 
