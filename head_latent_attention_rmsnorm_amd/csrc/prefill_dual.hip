@@ -186,7 +186,7 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + bh * (size_t)DV * a.v_ld, (uint32_t)DV * (uint32_t)a.v_ld * 2u);
     __amdgpu_buffer_rsrc_t rs[LPW];
     uint32_t voff[LPW], vstep[LPW];
-  #pragma unroll
+#pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int bi = wave + NW * i;
       if (bi < KBLK) {
@@ -216,14 +216,14 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
     }
     auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
       const uint32_t key0 = (uint32_t)(kt * BN);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < LPW; ++i) lds_load16(rs[i], &smem[buf][(wave + NW * i) * 64], voff[i] + key0 * vstep[i]);
     };
 
     // rotary positions of the lane's two query rows (looked up first: with
     // positions given, the wait for them then covers nothing else)
     int prow[2];
-  #pragma unroll
+#pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int tq = qlo + 32 * r + l32;
       prow[r] = a.pos ? a.pos[(size_t)b * T + (tq < T ? tq : 0)] : past + tq;
@@ -247,15 +247,15 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
     u32x4 qf[2][QC];
     f32x4 cw[2][RC], sw[2][RC];
     const int pairing = a.pairing;
-  #pragma unroll
+#pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int tq = qlo + 32 * r + l32;
       const int trow = tq < T ? tq : 0;
       const int p = prow[r];
       const uint16_t* qrow = qg + (size_t)trow * DQK;
-  #pragma unroll
+#pragma unroll
       for (int c = 0; c < QC; ++c) qf[r][c] = *reinterpret_cast<const u32x4*>(qrow + 16 * c + 8 * g);
-  #pragma unroll
+#pragma unroll
       for (int k = 0; k < RC; ++k) {
         // first pair of run k: half pairing, chunks k/2 and k/2 + RC/2, its
         // (k&1)-th four pairs; interleaved, chunk k
@@ -264,23 +264,23 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
         sw[r][k] = *reinterpret_cast<const f32x4*>(a.sin + (size_t)p * (DR / 2) + pi);
       }
     }
-  #pragma unroll
+#pragma unroll
     for (int r = 0; r < 2; ++r) {
       if (qlo + 32 * r + l32 >= T) {
-  #pragma unroll
+#pragma unroll
         for (int c = 0; c < QC; ++c) qf[r][c] = u32x4{0u, 0u, 0u, 0u};
       }
       auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
       auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
       u32x4 rot[RC];
       if (!pairing) {
-  #pragma unroll
+#pragma unroll
         for (int cc = 0; cc < RC; ++cc) {
           const bool first = cc < RC / 2;
           const u32x4 x = qf[r][DN / 16 + cc], y = qf[r][DN / 16 + (first ? cc + RC / 2 : cc - RC / 2)];
           const int k0 = 2 * (cc % (RC / 2));
           const float sgn = first ? -1.0f : 1.0f;
-  #pragma unroll
+#pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
             const f32x4 cs = cw[r][k0 + e2 / 2], sn = sw[r][k0 + e2 / 2];
             const int i0 = 2 * (e2 % 2);
@@ -289,22 +289,22 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
           }
         }
       } else {
-  #pragma unroll
+#pragma unroll
         for (int cc = 0; cc < RC; ++cc) {
           const u32x4 x = qf[r][DN / 16 + cc];
-  #pragma unroll
+#pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
             const float cs = cw[r][cc][e2], sn = sw[r][cc][e2];
             rot[cc][e2] = ET::pack2((lo(x[e2]) * cs - hi(x[e2]) * sn) * qmul, (hi(x[e2]) * cs + lo(x[e2]) * sn) * qmul);
           }
         }
       }
-  #pragma unroll
+#pragma unroll
       for (int c = 0; c < QC; ++c) {
         if (c >= DN / 16) {
           qf[r][c] = rot[c - DN / 16];
         } else if (FOLD || ET::code != BF16::code) {
-  #pragma unroll
+#pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) qf[r][c][e2] = ET::pack2(lo(qf[r][c][e2]) * qmul, hi(qf[r][c][e2]) * qmul);
         }
       }
@@ -312,22 +312,22 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
 
     // lane's read offsets within an operand group for each k-step position
     int rdk[SWK], rdv[SWV];
-  #pragma unroll
+#pragma unroll
     for (int c = 0; c < SWK; ++c) rdk[c] = frag_read0<SWK>(l32, g) ^ (32 * c);
-  #pragma unroll
+#pragma unroll
     for (int c = 0; c < SWV; ++c) rdv[c] = frag_read0<SWV>(l32, g) ^ (32 * c);
 
     // ---- running state per block
     f32x16 oacc[2][NO];
-  #pragma unroll
+#pragma unroll
     for (int r = 0; r < 2; ++r)
-  #pragma unroll
+#pragma unroll
       for (int d = 0; d < NO; ++d)
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 16; ++i) oacc[r][d][i] = 0.f;
-  #pragma unroll
+#pragma unroll
     for (int r = 0; r < 2; ++r)
-  #pragma unroll
+#pragma unroll
       for (int d = 0; d < NO; ++d) in_agpr(oacc[r][d]);
     float m_ref[2] = {0.f, 0.f};
     float lsum[2] = {0.f, 0.f};
@@ -335,9 +335,9 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
     // fp16 mode: -m_ref broadcast over an accumulator; every score chain starts
     // from it, so the scores leave the MFMA as exp2 arguments
     f32x16 negm[2];
-  #pragma unroll
+#pragma unroll
     for (int r = 0; r < 2; ++r) {
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < 16; ++i) negm[r][i] = 0.f;
       in_agpr(negm[r]);
     }
@@ -364,7 +364,7 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
           sacc[j][r] = ET::mma(f, qf[r][0], negm[r]);
         } else {
           f32x16 z;
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 16; ++e) z[e] = 0.f;
           sacc[j][r] = ET::mma(f, qf[r][0], z);
         }
@@ -392,7 +392,7 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
     auto copy_half = [&](int j, int r, int hh) __attribute__((always_inline)) {
       in_agpr(sacc[j][r]);  // holds the reads at this point
       f32x8 t;
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < 8; ++i) t[i] = sacc[j][r][8 * hh + i];
       in_vgpr(t);
       sv[j][r][hh] = t;
@@ -423,7 +423,7 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
     };
     // scores [v0, v1) of sub-tile j
     auto scores = [&](int j, int v0, int v1, int key0, bool diag) __attribute__((always_inline)) {
-  #pragma unroll
+#pragma unroll
       for (int v = v0; v < v1; ++v) score(j, v, key0, diag);
     };
 
@@ -437,10 +437,10 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
     auto check = [&](int j, bool pend, int key0, bool diag) __attribute__((always_inline)) {
       if (__any(!ref_set || ts[j][0] > kSumLimD || ts[j][1] > kSumLimD)) {
         float shift[2];
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < 2; ++r) {
           float mx = -INFINITY;
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, prepped(j, r, i, key0, diag));
           mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
           const bool raise = !ref_set || mx > kSlackD;
@@ -448,12 +448,12 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
           const float alpha = (raise && ref_set) ? __builtin_amdgcn_exp2f(-mx) : 1.f;
           m_ref[r] += shift[r];
           lsum[r] *= alpha;
-  #pragma unroll
+#pragma unroll
           for (int d = 0; d < NO; ++d) {
             // pin the accumulators to their registers on both sides of the
             // rescale, so that their copies for it stay on this rare path
             in_agpr(oacc[r][d]);
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 16; ++i) oacc[r][d][i] *= alpha;
             in_agpr(oacc[r][d]);
           }
@@ -461,21 +461,21 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
             if (pend) {
               // kept in the accumulation registers, as the common path holds it
               in_agpr(sacc[1 - j][r]);
-  #pragma unroll
+#pragma unroll
               for (int i = 0; i < 16; ++i) sacc[1 - j][r][i] -= shift[r];
               in_agpr(sacc[1 - j][r]);
             }
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 16; ++i) negm[r][i] = -m_ref[r];
             in_agpr(negm[r]);
           }
         }
         ref_set = true;
         // bf16 mode: prepped() now subtracts the moved reference itself
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < 2; ++r) {
           float t = 0.f;
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float c = FOLD ? shift[r] : 0.f;
             const float p0 = __builtin_amdgcn_exp2f(prepped(j, r, 2 * e, key0, diag) - c);
@@ -687,14 +687,14 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
       static_assert((CPR & (CPR - 1)) == 0 && CPR <= 64, "row swizzle needs a power-of-two chunk count");
       char* stile = reinterpret_cast<char*>(&smem[0][0]) + wave * (64 * DV * 2);
       float ltot[2];
-  #pragma unroll
+#pragma unroll
       for (int r = 0; r < 2; ++r) {
         ltot[r] = lsum[r] + __shfl_xor(lsum[r], 32, 64);
         const float inv = 1.0f / ltot[r];
         const int row = 32 * r + l32;
-  #pragma unroll
+#pragma unroll
         for (int d = 0; d < NO; ++d) {
-  #pragma unroll
+#pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
             const int c = d * 4 + r4;
             u32x2 o;
@@ -708,7 +708,7 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
       asm volatile("" ::: "memory");
       constexpr int RPI = 64 / CPR;
       const int ch = lane % CPR;
-  #pragma unroll
+#pragma unroll
       for (int rep = 0; rep < 64 / RPI; ++rep) {
         const int row = lane / CPR + RPI * rep;
         const u32x4 v = *reinterpret_cast<const u32x4*>(stile + row * (DV * 2) + ((ch ^ (row & (CPR - 1))) * 16));
@@ -716,7 +716,7 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
           __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(a.out + (bh * T + qlo + row) * DV + ch * 8));
       }
       if (a.lse && g == 0) {
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < 2; ++r) {
           const int tq = qlo + 32 * r + l32;
           if (tq < T) a.lse[bh * T + tq] = (m_ref[r] + log2f(ltot[r])) * kLn2D;
