@@ -415,8 +415,8 @@ mla_status mla_latent_cache_append(const mla_bf16* latent, const mla_bf16* gain,
 namespace {
 struct AbsorbedPlan {
   int S, tps;
-  size_t qa_bytes, po_bytes, lse_bytes, ol_bytes;
-  size_t total() const { return qa_bytes + po_bytes + lse_bytes + ol_bytes; }
+  size_t qa_bytes, po_bytes, lse_bytes;
+  size_t total() const { return qa_bytes + po_bytes + lse_bytes; }
 };
 // Splits over the key axis: enough workgroups for the chip (about 256)
 // when the batch is small, each split a whole number of 64-key tiles.
@@ -436,7 +436,6 @@ AbsorbedPlan absorbed_plan(int32_t B, int32_t H, int32_t Lcap, int32_t num_split
   p.qa_bytes = round256((size_t)B * H * (mla::kLatentR + mla::kLatentDr) * 2);
   p.po_bytes = round256((size_t)B * p.S * H * mla::kLatentR * 2);
   p.lse_bytes = round256((size_t)B * p.S * H * 4);
-  p.ol_bytes = round256((size_t)B * H * mla::kLatentR * 2);
   return p;
 }
 }  // namespace
@@ -470,7 +469,6 @@ mla_status mla_decode_absorbed(const mla_bf16* q, const mla_bf16* W, const mla_b
   uint16_t* qa = reinterpret_cast<uint16_t*>(ws);
   uint16_t* part_o = reinterpret_cast<uint16_t*>(ws + plan.qa_bytes);
   float* part_lse = reinterpret_cast<float*>(ws + plan.qa_bytes + plan.po_bytes);
-  uint16_t* o_lat = reinterpret_cast<uint16_t*>(ws + plan.qa_bytes + plan.po_bytes + plan.lse_bytes);
   clear_stale_error();
   const float kLog2e = 1.4426950408889634f;
   mla::AbsorbArgs aa{q, w_ukt, q_pos, cos, sin, table_len, B, H, Dn, Dr, pairing, scale * kLog2e, qa};
@@ -479,11 +477,8 @@ mla_status mla_decode_absorbed(const mla_bf16* q, const mla_bf16* W, const mla_b
   mla::LatentAttnArgs la{qa, cache, seq_len, part_o, part_lse, B, H, Lcap, plan.S, plan.tps};
   e = mla::launch_latent_attn(la, stream);
   if (e != hipSuccess) return MLA_ERR_HIP;
-  mla::LatentCombineArgs ca{part_o, part_lse, o_lat, B, H, plan.S};
-  e = mla::launch_latent_combine(ca, stream);
-  if (e != hipSuccess) return MLA_ERR_HIP;
-  mla::UnabsorbArgs ua{o_lat, W, out, B, H, Dn, Dv};
-  return hip_status(mla::launch_unabsorb(ua, stream));
+  mla::CombineUnabsorbArgs cu{part_o, part_lse, W, out, B, H, plan.S, Dn, Dv};
+  return hip_status(mla::launch_combine_unabsorb(cu, stream));
 }
 
 mla_status mla_decode_latent_expanded(const mla_bf16* q, const mla_bf16* W, const uint16_t* cache,

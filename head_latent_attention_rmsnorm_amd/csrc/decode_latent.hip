@@ -11,7 +11,7 @@
 //   q_lat[h]  = W_uk[h]^T q_nope[h]                       (absorb_q_kernel)
 //   s_s       = scale * (q_lat[h] . c_s + rot(q_pe[h]) . k_s)
 //   o_lat[h]  = sum_s softmax(s)_s c_s                    (latent_attn_kernel)
-//   out[h]    = W_uv[h] o_lat[h]         (latent_combine_kernel, unabsorb_kernel)
+//   out[h]    = W_uv[h] o_lat[h]                         (combine_unabsorb_kernel)
 // which equals attention over the expanded keys [W_uk c_s | k_s] and values
 // W_uv c_s. Every head reads the same 576-wide cache rows, so one workgroup
 // serves 64 heads from one copy of each key tile in LDS.
@@ -28,9 +28,9 @@
 //    stored as one fp16 row of 576, so scores leave the MFMA in log2 units.
 //  - latent_attn_kernel: split-K flash decoding over 64-key tiles, described
 //    at the kernel.
-//  - latent_combine_kernel: merges the split partials with the log-sum-exp
-//    rule into the fp16 latent aggregate o_lat.
-//  - unabsorb_kernel: o_lat times W_uv on fp16 MFMA.
+//  - combine_unabsorb_kernel: merges the split partials with the
+//    log-sum-exp rule into the fp16 latent aggregate o_lat (in LDS) and
+//    multiplies it by W_uv on fp16 MFMA, in one launch.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -580,85 +580,117 @@ hipError_t launch_latent_attn(const LatentAttnArgs& a, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// o_lat[b][h] = sum_s w_s o_s[b][h] with w_s = 2^(lse_s - lse) (the split
-// outputs are normalised, so the weights are the splits' shares of the row
-// sum), fp16 out. One thread per 8 latent columns of one (b, h). The first
-// split holds row 0 of every sequence, so the largest lse is finite.
-__global__ void __launch_bounds__(256) latent_combine_kernel(LatentCombineArgs a) {
-  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long)a.B * a.H * (LR / 8)) return;
-  const int c8 = (int)(idx % (LR / 8));
-  const long bh = idx / (LR / 8);
-  const int h = (int)(bh % a.H), b = (int)(bh / a.H);
-  const float* lse = a.part_lse + (size_t)b * a.S * a.H + h;
-  float mx = -INFINITY;
-  for (int s = 0; s < a.S; ++s) mx = fmaxf(mx, lse[(size_t)s * a.H]);
-  float v[8];
+// The merge and the value product in one launch: out[b][h] = W_uv[h] o_lat
+// with o_lat[b][h] = sum_s w_s o_s[b][h] / sum_s w_s, w_s = 2^(lse_s - max)
+// (the split outputs are normalised, so the weights are the splits' shares
+// of the row sum; the first split holds row 0 of every sequence, so the
+// largest lse is finite), never stored. Workgroup (h, CU_SEQ sequences),
+// 4 waves:
+//  1. merge: wave w merges sequences w, w+4 of the block, lane i its latent
+//     columns 8i..8i+7; the fp16 rows go to LDS (16-byte chunk x of row b at
+//     x ^ b, so the MFMA reads of 8 rows spread over 8 chunk slots);
+//  2. product: wave w computes output columns 32 db.. for db = w, w+4, ..
+//     < Dv/32 on fp16 MFMA, A = the o_lat rows (rows past the block's
+//     sequences are zero), B = W_uv's rows (bf16 -> fp16).
+// The 4 workgroups of one head share an XCD (grid x = head), so W_uv[h]
+// comes from HBM once.
+namespace {
+constexpr int CU_SEQ = 8;  // sequences per workgroup
+}
+__global__ void __launch_bounds__(256) combine_unabsorb_kernel(CombineUnabsorbArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t ol[CU_SEQ * LR];
+  const int h = blockIdx.x, b0 = blockIdx.y * CU_SEQ;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int ndb = a.Dv / 32;
+  // this wave's first W_uv rows go out first: their latency overlaps the merge
+  u32x4 wv[LR / 16];
+  if (wave < ndb) {
+    const uint16_t* wrow = a.W + ((size_t)h * (a.Dn + a.Dv) + a.Dn + wave * 32 + l32) * LR;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = 0.f;
-  float tot = 0.f;
-  const uint16_t* po = a.part_o + ((size_t)b * a.S * a.H + h) * LR + 8 * c8;
-#pragma unroll 4
-  for (int s = 0; s < a.S; ++s) {
-    // an empty split has lse -inf (weight 0) and zero rows
-    const float w = exp2f(lse[(size_t)s * a.H] - mx);
-    tot += w;
-    const u32x4 o = *reinterpret_cast<const u32x4*>(po + (size_t)s * a.H * LR);
+    for (int c = 0; c < LR / 16; ++c) wv[c] = *reinterpret_cast<const u32x4*>(wrow + 16 * c + 8 * g);
+  }
+  // merge, 8 splits per round: all of a round's loads are issued before its
+  // arithmetic
+  constexpr int SB = 8;
+  for (int bl = wave; bl < CU_SEQ; bl += 4) {
+    const int b = b0 + bl;
+    u32x4 r = {0u, 0u, 0u, 0u};
+    if (b < a.B) {
+      const float* lse = a.part_lse + (size_t)b * a.S * a.H + h;
+      const uint16_t* po = a.part_o + ((size_t)b * a.S * a.H + h) * LR + 8 * lane;
+      // running maximum over the rounds (the first split holds row 0 of
+      // every sequence, so it is finite after the first round)
+      float mx = -INFINITY;
+      float v[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[2 * e] += w * F16::lo(o[e]);
-      v[2 * e + 1] += w * F16::hi(o[e]);
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+      float tot = 0.f;
+      for (int s0 = 0; s0 < a.S; s0 += SB) {
+        u32x4 o[SB];
+        float l[SB];
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+          const bool in = s0 + k < a.S;
+          o[k] = in ? *reinterpret_cast<const u32x4*>(po + (size_t)(s0 + k) * a.H * LR) : u32x4{0u, 0u, 0u, 0u};
+          l[k] = in ? lse[(size_t)(s0 + k) * a.H] : -INFINITY;
+        }
+        float mr = mx;
+#pragma unroll
+        for (int k = 0; k < SB; ++k) mr = fmaxf(mr, l[k]);
+        const float sc = s0 == 0 ? 0.f : exp2f(mx - mr);
+        mx = mr;
+        tot *= sc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= sc;
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+          // an empty split has lse -inf (weight 0) and zero rows
+          const float w = exp2f(l[k] - mx);
+          tot += w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] += w * F16::lo(o[k][e]);
+            v[2 * e + 1] += w * F16::hi(o[k][e]);
+          }
+        }
+      }
+      const float it = 1.0f / tot;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = pack2h(v[2 * e] * it, v[2 * e + 1] * it);
+    }
+    *reinterpret_cast<u32x4*>(ol + bl * LR + 8 * (lane ^ bl)) = r;
+  }
+  __syncthreads();
+  for (int db = wave; db < ndb; db += 4) {
+    if (db != wave) {
+      const uint16_t* wrow = a.W + ((size_t)h * (a.Dn + a.Dv) + a.Dn + db * 32 + l32) * LR;
+#pragma unroll
+      for (int c = 0; c < LR / 16; ++c) wv[c] = *reinterpret_cast<const u32x4*>(wrow + 16 * c + 8 * g);
+    }
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < LR / 16; ++c) {
+      const int x = 2 * c + g;  // 16-byte chunk of the o_lat row
+      const u32x4 av =
+          l32 < CU_SEQ ? *reinterpret_cast<const u32x4*>(ol + l32 * LR + 8 * (x ^ l32)) : u32x4{0u, 0u, 0u, 0u};
+      acc = mma_f16(av, bf16x8_to_f16x8(wv[c]), acc);
+    }
+    // C[row][col]: lane holds column db*32 + l32, rows 8*(i>>2) + 4g + (i&3)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int bl = 8 * (i >> 2) + 4 * g + (i & 3);
+      if (bl < CU_SEQ && b0 + bl < a.B) a.out[((size_t)(b0 + bl) * a.H + h) * a.Dv + db * 32 + l32] = f2bf(acc[i]);
     }
   }
-  const float it = 1.0f / tot;
-  u32x4 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) r[e] = pack2h(v[2 * e] * it, v[2 * e + 1] * it);
-  *reinterpret_cast<u32x4*>(a.o_lat + (size_t)bh * LR + 8 * c8) = r;
 }
 
-hipError_t launch_latent_combine(const LatentCombineArgs& a, hipStream_t stream) {
-  const long n = (long)a.B * a.H * (LR / 8);
-  hipLaunchKernelGGL(latent_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
-
-// out[b][h] = W_uv[h] o_lat[b][h]: per head a [B x 512] x [512 x Dv] product
-// on fp16 MFMA. Wave (32 output columns, h, 32 sequences): the A operand is
-// o_lat (8 consecutive latent columns per lane), the B operand W_uv's row
-// (bf16 -> fp16, exact for weights in the fp16 range); the 32 k-steps'
-// loads are issued in two groups of 16 ahead of their MFMAs.
-__global__ void __launch_bounds__(64) unabsorb_kernel(UnabsorbArgs a) {
-  const int db = blockIdx.x, h = blockIdx.y, b0 = blockIdx.z * 32;
-  const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
-  const uint16_t* wrow = a.W + ((size_t)h * (a.Dn + a.Dv) + a.Dn + db * 32 + l32) * LR;
-  const int b = min(b0 + l32, a.B - 1);
-  const uint16_t* orow = a.o_lat + ((size_t)b * a.H + h) * LR;
-  f32x16 acc;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-  for (int c0 = 0; c0 < LR / 16; c0 += 16) {
-    u32x4 av[16], wv[16];
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      av[c] = *reinterpret_cast<const u32x4*>(orow + 16 * (c0 + c) + 8 * g);
-      wv[c] = *reinterpret_cast<const u32x4*>(wrow + 16 * (c0 + c) + 8 * g);
-    }
-#pragma unroll
-    for (int c = 0; c < 16; ++c) acc = mma_f16(av[c], bf16x8_to_f16x8(wv[c]), acc);
-  }
-  // C[b][col]: lane holds column db*32 + l32, rows 8*(i>>2) + 4g + (i&3)
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int bb = b0 + 8 * (i >> 2) + 4 * g + (i & 3);
-    if (bb < a.B) a.out[((size_t)bb * a.H + h) * a.Dv + db * 32 + l32] = f2bf(acc[i]);
-  }
-}
-
-hipError_t launch_unabsorb(const UnabsorbArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.Dv / 32), (unsigned)a.H, (unsigned)((a.B + 31) / 32));
-  hipLaunchKernelGGL(unabsorb_kernel, grid, dim3(64), 0, stream, a);
+hipError_t launch_combine_unabsorb(const CombineUnabsorbArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.H, (unsigned)((a.B + CU_SEQ - 1) / CU_SEQ));
+  hipLaunchKernelGGL(combine_unabsorb_kernel, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -169,21 +169,14 @@ struct LatentAttnArgs {
 };
 hipError_t launch_latent_attn(const LatentAttnArgs& a, hipStream_t stream);
 
-struct LatentCombineArgs {
-  const uint16_t* part_o;
-  const float* part_lse;
-  uint16_t* o_lat;  // [B, H, 512] fp16
-  int B, H, S;
+struct CombineUnabsorbArgs {
+  const uint16_t* part_o;  // [B, S, H, 512] fp16 split outputs
+  const float* part_lse;   // [B, S, H] log2-domain
+  const uint16_t* W;       // [H*(Dn+Dv), 512] bf16
+  uint16_t* out;           // [B, H, 1, Dv] bf16
+  int B, H, S, Dn, Dv;
 };
-hipError_t launch_latent_combine(const LatentCombineArgs& a, hipStream_t stream);
-
-struct UnabsorbArgs {
-  const uint16_t* o_lat;  // [B, H, 512] fp16
-  const uint16_t* W;      // [H*(Dn+Dv), 512] bf16
-  uint16_t* out;          // [B, H, 1, Dv] bf16
-  int B, H, Dn, Dv;
-};
-hipError_t launch_unabsorb(const UnabsorbArgs& a, hipStream_t stream);
+hipError_t launch_combine_unabsorb(const CombineUnabsorbArgs& a, hipStream_t stream);
 
 // latent cache -> contiguous latent rows [B*Lcap, R] and the rotated key
 // broadcast into columns Dn.. of the expanded key cache [B, H, Lcap, Dn+Dr]

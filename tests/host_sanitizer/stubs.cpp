@@ -123,13 +123,9 @@ hipError_t launch_latent_attn(const LatentAttnArgs& a, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }
-hipError_t launch_latent_combine(const LatentCombineArgs& a, hipStream_t) {
-  NEED(a.part_o && a.part_lse && a.o_lat && a.S >= 1);
-  ++g_launches;
-  return hipSuccess;
-}
-hipError_t launch_unabsorb(const UnabsorbArgs& a, hipStream_t) {
-  NEED(a.o_lat && a.W && a.out && a.B >= 1 && a.H >= 1);
+hipError_t launch_combine_unabsorb(const CombineUnabsorbArgs& a, hipStream_t) {
+  NEED(a.part_o && a.part_lse && a.W && a.out && a.B >= 1 && a.H >= 1 && a.S >= 1 && a.S <= kMaxLatentSplits);
+  NEED(a.Dv >= 32 && a.Dv % 32 == 0);
   ++g_launches;
   return hipSuccess;
 }
