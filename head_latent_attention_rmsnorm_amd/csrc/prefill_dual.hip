@@ -127,7 +127,10 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
   static_assert(NW * 64 * DV * 2 <= NBLK * 1024 * 2, "the output tiles fit in the tile buffers");
 
   static_assert(NBUF == 2 || NBUF == 3, "double or triple buffered tiles");
-  __shared__ __attribute__((aligned(16))) u32x4 smem[NBUF][NBLK * 64];
+  // NBUF tile buffers and one more: at the start of an item the waves' query
+  // rows are staged from buffer 1 on (2 QC KB per wave)
+  static_assert(NBLK * 1024 + NW * 2 * QC * 1024 <= (NBUF + 1) * NBLK * 1024, "query staging fits");
+  __shared__ __attribute__((aligned(16))) u32x4 smem[NBUF + 1][NBLK * 64];
 
   const int HB = a.H * a.B;
   // Persistent: one workgroup per CU works through the (b, h, 256-row) items
@@ -220,41 +223,58 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
       for (int i = 0; i < LPW; ++i) lds_load16(rs[i], &smem[buf][(wave + NW * i) * 64], voff[i] + key0 * vstep[i]);
     };
 
-    // rotary positions of the lane's two query rows (looked up first: with
-    // positions given, the wait for them then covers nothing else)
+    // rotary positions of the lane's two query rows. Given positions are
+    // looked up and waited for inside their own branch: a load still pending
+    // where the branches join would make the other branch wait for every
+    // memory operation in flight, the previous item's output stores included.
     int prow[2];
+    if (a.pos) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int tq = qlo + 32 * r + l32;
-      prow[r] = a.pos ? a.pos[(size_t)b * T + (tq < T ? tq : 0)] : past + tq;
-      prow[r] = min(max(prow[r], 0), a.table_len - 1);
+      for (int r = 0; r < 2; ++r) {
+        const int tq = qlo + 32 * r + l32;
+        prow[r] = a.pos[(size_t)b * T + (tq < T ? tq : 0)];
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r) asm volatile("" : "+v"(prow[r]));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) prow[r] = past + qlo + 32 * r + l32;
     }
-
-    // the first tile's loads go out before the query's, so that both
-    // latencies overlap
-    issue(0, 0);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) prow[r] = min(max(prow[r], 0), a.table_len - 1);
 
     // ---- prologue: rotated (and in fp16 mode pre-scaled) query fragments of
-    // both blocks. Every load goes out before any arithmetic: the query chunks
-    // of both blocks, then the cos / sin of the lane's rotary pairs, so the
-    // whole prologue waits for one memory round trip. Rotary chunk cc (16
+    // both blocks. Every load goes out before any arithmetic, so the whole
+    // prologue waits for one memory round trip: the wave's 64 query rows
+    // (contiguous in memory) land in LDS as the operand image the key tiles
+    // use, each LDS-direct load bringing eight whole 128-byte row segments
+    // (rows past the sequence read as zeros); then the cos / sin of the
+    // lane's rotary pairs; then the first tile. Rotary chunk cc (16
     // dims, dims 8g..8g+7 in this lane) pairs dims within the chunk
     // (interleaved: 4 pairs) or with chunk cc +- RC/2 (half: 8 pairs, the
     // partner dims in the same lane); either way a lane touches DR/4 pairs,
     // DR/16 runs of four.
     constexpr int RC = DR / 16;
     static_assert(DN % 16 == 0 && DR % 32 == 0, "rotary chunks of 16 dims, two halves");
+    static_assert(SWK == 4, "query staging in groups of four k-steps");
+    const char* qimg = reinterpret_cast<const char*>(&smem[1][0]) + wave * (2 * QC * 1024);
+    {
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg, (uint32_t)T * DQK * 2u);
+#pragma unroll
+      for (int bi = 0; bi < 2 * QC; ++bi) {
+        const int r = bi / QC, cq = bi % QC;
+        int rr, x;
+        frag_slot<SWK>(cq % SWK, lane, rr, x);
+        const int col = (cq / SWK) * (16 * SWK) + 8 * x;
+        lds_load16(rq, const_cast<char*>(qimg) + bi * 1024, (uint32_t)((qlo + 32 * r + rr) * DQK + col) * 2u);
+      }
+    }
     u32x4 qf[2][QC];
     f32x4 cw[2][RC], sw[2][RC];
     const int pairing = a.pairing;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int tq = qlo + 32 * r + l32;
-      const int trow = tq < T ? tq : 0;
       const int p = prow[r];
-      const uint16_t* qrow = qg + (size_t)trow * DQK;
-#pragma unroll
-      for (int c = 0; c < QC; ++c) qf[r][c] = *reinterpret_cast<const u32x4*>(qrow + 16 * c + 8 * g);
 #pragma unroll
       for (int k = 0; k < RC; ++k) {
         // first pair of run k: half pairing, chunks k/2 and k/2 + RC/2, its
@@ -264,12 +284,25 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
         sw[r][k] = *reinterpret_cast<const f32x4*>(a.sin + (size_t)p * (DR / 2) + pi);
       }
     }
+    // the first tile's loads go out last: the wait below leaves them in flight
+    issue(0, 0);
+    // lane's read offsets within an operand group for each k-step position
+    int rdk[SWK], rdv[SWV];
+#pragma unroll
+    for (int c = 0; c < SWK; ++c) rdk[c] = frag_read0<SWK>(l32, g) ^ (32 * c);
+#pragma unroll
+    for (int c = 0; c < SWV; ++c) rdv[c] = frag_read0<SWV>(l32, g) ^ (32 * c);
+    // this wave's staging loads (and the cos / sin) have landed: vmcnt(LPW)
+    static_assert(LPW < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | LPW);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int c = 0; c < QC; ++c)
+        qf[r][c] = *reinterpret_cast<const u32x4*>(qimg + (r * QC + (c / SWK) * SWK) * 1024 + rdk[c % SWK]);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      if (qlo + 32 * r + l32 >= T) {
-#pragma unroll
-        for (int c = 0; c < QC; ++c) qf[r][c] = u32x4{0u, 0u, 0u, 0u};
-      }
       auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
       auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
       u32x4 rot[RC];
@@ -309,13 +342,6 @@ __global__ void __launch_bounds__(256, 1) prefill_dual_kernel(PrefillArgs a, int
         }
       }
     }
-
-    // lane's read offsets within an operand group for each k-step position
-    int rdk[SWK], rdv[SWV];
-#pragma unroll
-    for (int c = 0; c < SWK; ++c) rdk[c] = frag_read0<SWK>(l32, g) ^ (32 * c);
-#pragma unroll
-    for (int c = 0; c < SWV; ++c) rdv[c] = frag_read0<SWV>(l32, g) ^ (32 * c);
 
     // ---- running state per block
     f32x16 oacc[2][NO];
